@@ -1,0 +1,100 @@
+"""Seeded synthetic attention inputs.
+
+This module only draws random numbers: Q, K, V with the shapes and value
+distributions of the attention workloads below, rounded to the storage type
+the kernels read, and the sparse +-20 outlier substitution used for the FP8
+workload.  It holds none of the attention or quantisation arithmetic, so both
+the CPU oracle's tests and the GPU path can take their inputs from it.
+
+Draw order for one workload (fixed, so every consumer sees identical tensors):
+Q, K, V from N(0, std^2) in float32; then, for the outlier workload only, a
+Bernoulli mask for Q, the signs for Q, a Bernoulli mask for K and the signs
+for K.  Selected coordinates are replaced (not added to) by +-outlier_value.
+The float32 draws are finally rounded (round to nearest even) to bfloat16
+for every workload whose source precision is bf16; the fp32 workload keeps
+the float32 draws.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str              # "f32" | "bf16" | "fp8" (fp8: bf16 source, quantised on the GPU)
+    seed: int
+    std: float = 1.0
+    outlier_frac: float = 0.0
+    outlier_value: float = 20.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """Attention FLOPs counted the usual way: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    def with_shape(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The workloads: a tiny fp32 case, bf16 causal and non-causal cases, the FP8
+# causal case with outliers, its bf16 twin at the same 8k shape, and a
+# 32k-token layer shaped like a 7B model's attention (32 heads of 128).
+WORKLOADS = {
+    "f32_tiny": Workload("f32_tiny", 1, 1, 128, 64, False, "f32", seed=1001),
+    "bf16_causal_2k": Workload("bf16_causal_2k", 4, 16, 2048, 128, True, "bf16", seed=1002),
+    "bf16_d64_4k": Workload("bf16_d64_4k", 8, 32, 4096, 64, False, "bf16", seed=1003),
+    "fp8_causal_8k": Workload("fp8_causal_8k", 2, 16, 8192, 128, True, "fp8", seed=1004,
+                              outlier_frac=0.001, outlier_value=20.0),
+    "bf16_causal_8k": Workload("bf16_causal_8k", 2, 16, 8192, 128, True, "bf16", seed=1006),
+    "bf16_causal_32k": Workload("bf16_causal_32k", 1, 32, 32768, 128, True, "bf16", seed=1005, std=0.5),
+}
+
+# The 8k-token causal bf16 workload is the headline throughput point.
+HEADLINE = "bf16_causal_8k"
+
+
+def _outliers(x: torch.Tensor, g: torch.Generator, frac: float, value: float) -> torch.Tensor:
+    mask = torch.rand(x.shape, generator=g) < frac
+    sign = torch.randint(0, 2, x.shape, generator=g, dtype=torch.int8).to(torch.float32) * 2.0 - 1.0
+    return torch.where(mask, sign * value, x)
+
+
+def make_qkv(w: Workload, seed: int | None = None):
+    """Return (q, k, v) as contiguous CPU tensors of shape [B, H, N, d].
+
+    dtype float32 for the fp32 workload, bfloat16 otherwise (the FP8 workload's
+    tensors are the bf16 source values that the quantiser reads).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32) * w.std
+    k = torch.randn(shape, generator=g, dtype=torch.float32) * w.std
+    v = torch.randn(shape, generator=g, dtype=torch.float32) * w.std
+    if w.outlier_frac > 0.0:
+        q = _outliers(q, g, w.outlier_frac, w.outlier_value)
+        k = _outliers(k, g, w.outlier_frac, w.outlier_value)
+    if w.dtype in ("bf16", "fp8"):
+        q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def custom(B: int, H: int, N: int, d: int, causal: bool, dtype: str = "bf16", seed: int = 7,
+           std: float = 1.0, outlier_frac: float = 0.0) -> Workload:
+    """An ad-hoc workload (edge shapes in tests) drawn by the same recipe."""
+    return Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, causal, dtype, seed=seed, std=std,
+                    outlier_frac=outlier_frac)

@@ -1,0 +1,22 @@
+"""CPU oracle for the fused attention path: plain, slow, float64.
+
+TEST INFRASTRUCTURE ONLY.  Importers allowed: the tests under ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``.  The
+HIP library and its Python binding never import or call anything here, and
+nothing here imports them: the two implementations share no code.
+
+  attention.attention  -- softmax(scale Q K^T + causal mask) V and LSE, by the
+                          definition (full score rows, float64)
+  fp8.*                -- Sylvester Hadamard matrix, E4M3 encode/decode from
+                          the bit layout, per-block quantisation, and attention
+                          on dequantised FP8 operands
+
+Every function is pinned by tests against closed forms, special cases,
+brute force and library routines; none is marked "parity unpinned".
+"""
+from .attention import attention
+from .fp8 import (sylvester_hadamard, orthonormal_hadamard, e4m3_decode, e4m3_encode,
+                  quantize_blocks, dequantize_blocks, attention_fp8, E4M3_MAX, BLOCK)
+
+__all__ = ["attention", "sylvester_hadamard", "orthonormal_hadamard", "e4m3_decode", "e4m3_encode",
+           "quantize_blocks", "dequantize_blocks", "attention_fp8", "E4M3_MAX", "BLOCK"]

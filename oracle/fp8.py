@@ -1,0 +1,138 @@
+"""Plain fp64 emulation of the FP8 path with incoherent processing.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this module; the product path
+never calls it.  It shares no code with the GPU path (no table, constant or
+helper is common to both).
+
+What the pages fix ("FlashAttention-3 (PT)", section "Inovacoes tecnicas",
+item 3, low precision FP8 with incoherent processing; same list in the (SV)
+and (IT) versions):
+  1. before attention, Q and K are multiplied by a random orthogonal matrix,
+     for example a Hadamard matrix;
+  2. that spreads outlier coordinates over all coordinates;
+  3. then Q and K are quantised to FP8, with less error;
+  4. since the matrix is orthogonal it cancels in Q K^T, so the attention
+     result is unchanged.
+
+Readings where the pages are silent:
+  - the matrix is the Sylvester Hadamard matrix of order d (d = 128), natural
+    order, divided by sqrt(d) so it is orthogonal; the same matrix for every
+    head, applied over the head dimension (row vector x -> x H);
+  - FP8 is the OCP E4M3 "fn" format: 1 sign, 4 exponent (bias 7) and 3
+    mantissa bits, no infinities, one NaN pattern per sign (S.1111.111),
+    largest finite 448, subnormals m * 2^-9; conversion rounds to nearest,
+    ties to even, and clamps magnitudes above 448 to 448;
+  - scaling is per block: one scale per (batch, head, block of 128 tokens),
+    over all d coordinates; s = amax / 448, or s = 1 when the block is all
+    zero; the last block covers the remaining rows only; code = E4M3(y / s);
+    the scale is stored as float32 and dequantisation is code * s;
+  - V is quantised per block the same way, without the Hadamard matrix;
+  - inside attention P is quantised as E4M3(256 p) / 256 with p = exp(S - m)
+    relative to the row maximum; the row sum l uses the unquantised p.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+BLOCK = 128
+
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """The +-1 Hadamard matrix of order n (a power of two) by Sylvester's
+    doubling H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("order must be a power of two")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def orthonormal_hadamard(n: int) -> np.ndarray:
+    return sylvester_hadamard(n) / np.sqrt(n)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 byte, read from the bit layout s.eeee.mmm."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+# Magnitudes of the 127 non-negative finite codes 0x00..0x7E; they increase
+# strictly with the code, so the nearest value can be found by bisection.
+_MAGS = e4m3_decode(np.arange(0x7F))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round each value to the nearest E4M3 code, ties to the even code,
+    magnitudes above 448 clamped to 448, NaN to 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_MAGS, a, side="left").clip(0, 0x7E)       # first magnitude >= a
+    lo = (hi - 1).clip(0, 0x7E)
+    d_hi = _MAGS[hi] - a
+    d_lo = a - _MAGS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_blocks(x, hadamard: bool, block: int = BLOCK):
+    """Incoherent processing (optional) then per-block FP8 quantisation of a
+    [B, H, N, d] tensor.  Returns (codes uint8 [B,H,N,d], scales float32
+    [B,H,ceil(N/block)])."""
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    y = x @ orthonormal_hadamard(d) if hadamard else x
+    nb = -(-N // block)
+    codes = np.empty((B, H, N, d), dtype=np.uint8)
+    scales = np.empty((B, H, nb), dtype=np.float32)
+    for j in range(nb):
+        blk = y[:, :, j * block:(j + 1) * block, :]
+        amax = np.abs(blk).max(axis=(2, 3))
+        s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        codes[:, :, j * block:(j + 1) * block, :] = e4m3_encode(blk / s[:, :, None, None])
+        scales[:, :, j] = s.astype(np.float32)
+    return codes, scales
+
+
+def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
+    """code * (float32 scale of its block), in float64."""
+    vals = e4m3_decode(codes)
+    s = np.repeat(np.asarray(scales, dtype=np.float64), block, axis=2)[:, :, :vals.shape[2]]
+    return vals * s[..., None]
+
+
+def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p: bool = True,
+                  block: int = BLOCK):
+    """Attention on dequantised FP8 operands, with P itself quantised as
+    E4M3(256 p)/256 when ``quantize_p`` (l from the unquantised p).
+    Returns (O, LSE) in float64."""
+    q = dequantize_blocks(q8, qs, block)
+    k = dequantize_blocks(k8, ks, block)
+    v = dequantize_blocks(v8, vs, block)
+    B, H, N, d = q.shape
+    idx = np.arange(N)
+    o = np.empty((B, H, N, v.shape[3]))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                s = np.where(idx[None, :] > idx[:, None], -np.inf, s)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            pq = e4m3_decode(e4m3_encode(256.0 * p)) / 256.0 if quantize_p else p
+            o[b, h] = (pq @ v[b, h]) / l
+            lse[b, h] = (m + np.log(l))[:, 0]
+    return o, lse

@@ -1,0 +1,376 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-derived cases, closed forms and invariants of softmax attention,
+brute-force scalar loops, and library routines computing the same definition.
+CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def _expr(s):
+    return eval(s, {"__builtins__": {}}, {"ln": math.log, "exp": math.exp})
+
+
+# ---------------------------------------------------------------------------
+# hand-derived fixtures
+@pytest.mark.parametrize("causal", [False, True])
+def test_hand_derived_cases(causal):
+    cases = json.load(open(os.path.join(GOLDEN, "attention_hand.json")))["cases"]
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float64)
+        if c.get("q_is_ln3"):
+            q[:] = math.log(3.0)
+        k, v = np.array(c["k"], dtype=np.float64), np.array(c["v"], dtype=np.float64)
+        o, lse = attention(q[None, None], k[None, None], v[None, None], c["scale"], causal)
+        exp = c["causal" if causal else "noncausal"]
+        o_ref = np.array([[_expr(x) for x in row] for row in exp["o"]])
+        lse_ref = np.array([_expr(x) for x in exp["lse"]])
+        np.testing.assert_allclose(o[0, 0], o_ref, rtol=0, atol=1e-14, err_msg=c["name"])
+        np.testing.assert_allclose(lse[0, 0], lse_ref, rtol=0, atol=1e-14, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------------------
+# brute force: scalar loops with math.exp, no arrays
+def _brute(q, k, v, scale, causal):
+    N, d = len(q), len(q[0])
+    O, L = [], []
+    for i in range(N):
+        s = []
+        for j in range(N):
+            if causal and j > i:
+                continue
+            s.append((j, scale * sum(q[i][t] * k[j][t] for t in range(d))))
+        m = max(x for _, x in s)
+        w = [(j, math.exp(x - m)) for j, x in s]
+        l = sum(x for _, x in w)
+        O.append([sum(x * v[j][t] for j, x in w) / l for t in range(len(v[0]))])
+        L.append(m + math.log(l))
+    return O, L
+
+
+@pytest.mark.parametrize("N,d", [(1, 1), (2, 3), (5, 4), (7, 2), (8, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(N, d, causal):
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    scale = 0.7
+    o, lse = attention(q[None, None], k[None, None], v[None, None], scale, causal)
+    O, L = _brute(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(o[0, 0], np.array(O), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.array(L), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# closed forms named for the path
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    # with V = identity, O is the probability matrix itself
+    N, d = 37, 16
+    q, k = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    o, _ = attention(q[None, None], k[None, None], np.eye(N)[None, None], 0.3, causal)
+    p = o[0, 0]
+    assert np.all(p >= 0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    if causal:
+        assert np.all(p[np.triu_indices(N, 1)] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_v(causal):
+    N, d = 29, 8
+    q, v = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    k = np.tile(rng.standard_normal((1, d)), (N, 1))
+    scale = 0.5
+    o, lse = attention(q[None, None], k[None, None], v[None, None], scale, causal)
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = np.cumsum(v, axis=0) / cnt[:, None] if causal else np.tile(v.mean(axis=0), (N, 1))
+    np.testing.assert_allclose(o[0, 0], mean, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], scale * q @ k[0] + np.log(cnt), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_token_returns_v(causal):
+    q, k, v = (rng.standard_normal((3, 2, 1, 64)) for _ in range(3))
+    o, lse = attention(q, k, v, 0.125, causal)
+    np.testing.assert_array_equal(o, v)
+    np.testing.assert_allclose(lse, 0.125 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-14)
+
+
+def test_causal_first_row_is_v0():
+    q, k, v = (rng.standard_normal((2, 3, 50, 32)) for _ in range(3))
+    o, lse = attention(q, k, v, 0.2, True)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.2 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                               rtol=0, atol=1e-14)
+
+
+def test_scale_zero_is_uniform():
+    N, d = 40, 8
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    o, lse = attention(q, k, v, 0.0, False)
+    np.testing.assert_allclose(o[0, 0], np.tile(v[0, 0].mean(axis=0), (N, 1)), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], np.log(N), atol=1e-14)
+    o, lse = attention(q, k, v, 0.0, True)
+    np.testing.assert_allclose(o[0, 0], np.cumsum(v[0, 0], axis=0) / np.arange(1, N + 1)[:, None], atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.arange(1, N + 1)), atol=1e-14)
+
+
+def test_huge_scale_is_hardmax():
+    N, d = 33, 16
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    o, lse = attention(q, k, v, 1e6, False)
+    s = q[0, 0] @ k[0, 0].T
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    np.testing.assert_allclose(o[0, 0], v[0, 0][s.argmax(axis=1)], atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], 1e6 * s.max(axis=1), rtol=1e-15)
+
+
+def test_permutation_equivariance():
+    N, d = 45, 8
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    o, lse = attention(q, k, v, 0.4, False)
+    pk, pq = rng.permutation(N), rng.permutation(N)
+    o2, lse2 = attention(q[:, :, pq], k[:, :, pk], v[:, :, pk], 0.4, False)
+    np.testing.assert_allclose(o2, o[:, :, pq], atol=1e-13)
+    np.testing.assert_allclose(lse2, lse[:, :, pq], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    # K <- K + 1 c^T adds scale*q_i.c to row i: O unchanged, LSE_i shifted by it
+    N, d = 31, 8
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    c = rng.standard_normal(d)
+    o, lse = attention(q, k, v, 0.6, causal)
+    o2, lse2 = attention(q, k + c, v, 0.6, causal)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse + 0.6 * (q @ c), atol=1e-12)
+
+
+def test_split_keys_merge_identity():
+    # attention over two disjoint key sets, merged through their LSEs, equals
+    # attention over all keys (the identity the online softmax accumulates by)
+    N, d, a = 60, 16, 23
+    q, k, v = (rng.standard_normal((2, 2, N, d)) for _ in range(3))
+    o, lse = attention(q, k, v, 0.3, False)
+    o1, l1 = attention(q, k[:, :, :a], v[:, :, :a], 0.3, False)
+    o2, l2 = attention(q, k[:, :, a:], v[:, :, a:], 0.3, False)
+    m = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - m), np.exp(l2 - m)
+    np.testing.assert_allclose((w1[..., None] * o1 + w2[..., None] * o2) / (w1 + w2)[..., None], o, atol=1e-13)
+    np.testing.assert_allclose(m + np.log(w1 + w2), lse, atol=1e-13)
+
+
+def test_row_subset_matches_full():
+    N, d = 300, 16
+    q, k, v = (rng.standard_normal((1, 2, N, d)) for _ in range(3))
+    o, lse = attention(q, k, v, 0.25, True)
+    rows = np.array([0, 1, 77, 128, 299])
+    o2, lse2 = attention(q[:, :, rows], k, v, 0.25, True, q_index=rows)
+    np.testing.assert_allclose(o2, o[:, :, rows], atol=1e-14)
+    np.testing.assert_allclose(lse2, lse[:, :, rows], atol=1e-14)
+    o3, _ = attention(q, k, v, 0.25, True, row_band=64)          # banding does not change a row
+    np.testing.assert_allclose(o3, o, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 256, 511])
+def test_matches_torch_sdpa_fp64(N, causal):
+    d = 64
+    q, k, v = (torch.randn(2, 3, N, d, dtype=torch.float64, generator=torch.Generator().manual_seed(N)) for _ in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=0.125)
+    o, _ = attention(q.numpy(), k.numpy(), v.numpy(), 0.125, causal)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12)
+    s = 0.125 * (q @ k.transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    _, lse = attention(q.numpy(), k.numpy(), v.numpy(), 0.125, causal)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard
+def test_hadamard_matches_textbook_order8():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "hadamard8.txt")) if not l.startswith("#") and l.strip()]
+    np.testing.assert_array_equal(oracle.sylvester_hadamard(8), np.array(rows, dtype=np.float64))
+
+
+@pytest.mark.parametrize("n", [1, 2, 64, 128])
+def test_hadamard_orthogonal(n):
+    h = oracle.sylvester_hadamard(n)
+    assert set(np.unique(h)) <= {-1.0, 1.0}
+    np.testing.assert_array_equal(h @ h.T, n * np.eye(n))
+    hn = oracle.orthonormal_hadamard(n)
+    np.testing.assert_allclose(hn @ hn.T, np.eye(n), atol=1e-15)
+
+
+def test_incoherent_processing_leaves_qk_and_attention_unchanged():
+    # the orthogonal matrix cancels in Q K^T (pages: incoherent processing, step 4)
+    N, d = 1024, 128
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    for x in (q, k):
+        m = rng.random(x.shape) < 0.001
+        x[m] = 20.0 * np.sign(rng.standard_normal(m.sum()))
+    hn = oracle.orthonormal_hadamard(d)
+    s0 = q[0, 0] @ k[0, 0].T
+    s1 = (q[0, 0] @ hn) @ (k[0, 0] @ hn).T
+    assert np.abs(s1 - s0).max() <= 1e-11
+    o0, l0 = attention(q, k, v, d ** -0.5, True)
+    o1, l1 = attention(q @ hn, k @ hn, v, d ** -0.5, True)
+    np.testing.assert_allclose(o1, o0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# E4M3
+def test_e4m3_decode_anchors():
+    for line in open(os.path.join(GOLDEN, "e4m3_anchors.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code, val = line.split()
+        got = oracle.e4m3_decode(int(code, 16))
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert float(got) == float(val), code
+
+
+def test_e4m3_decode_matches_torch_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_e4m3_encode_roundtrip_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)), codes)
+    # ties go to the even code; values above 448 clamp; half the smallest subnormal ties to zero
+    assert oracle.e4m3_encode(1.0625) == 0x38
+    assert oracle.e4m3_encode(1.1875) == 0x3A
+    assert oracle.e4m3_encode(464.0) == 0x7E
+    assert oracle.e4m3_encode(1e9) == 0x7E
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00
+    assert oracle.e4m3_encode(3 * 2.0 ** -11) == 0x01
+    assert oracle.e4m3_encode(-1.0625) == 0xB8
+
+
+def test_e4m3_encode_matches_torch_cast():
+    x = np.concatenate([rng.standard_normal(400_000) * 50,
+                        rng.uniform(-448, 448, 300_000),
+                        rng.standard_normal(300_000) * 1e-2])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(x.astype(np.float32).astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# per-block quantisation
+def test_quantize_blocks_properties():
+    B, H, N, d = 2, 3, 300, 128                       # ragged last block (300 = 2*128 + 44)
+    x = rng.standard_normal((B, H, N, d))
+    x[0, 1, 128:256] = 0.0                              # an all-zero block
+    for had in (False, True):
+        codes, scales = oracle.quantize_blocks(x, had)
+        assert codes.shape == x.shape and scales.shape == (B, H, 3)
+        y = x @ oracle.orthonormal_hadamard(d) if had else x
+        assert scales[0, 1, 1] == 1.0 and np.all(codes[0, 1, 128:256] & 0x7F == 0)
+        deq = oracle.dequantize_blocks(codes, scales)
+        for b in range(B):
+            for h in range(H):
+                for j in range(3):
+                    blk = y[b, h, j * 128:(j + 1) * 128]
+                    amax = np.abs(blk).max()
+                    if amax == 0:
+                        continue
+                    s = amax / 448.0
+                    assert abs(scales[b, h, j] - s) <= 2.0 ** -24 * s
+                    # the amax element lands exactly on +-448
+                    i = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+                    assert codes[b, h, j * 128 + i[0], i[1]] & 0x7F == 0x7E
+                    # rounding error: half a step, relative 2^-4 for normals, 2^-10 s absolute below
+                    err = np.abs(deq[b, h, j * 128:(j + 1) * 128] - blk)
+                    bound = np.maximum(np.abs(blk) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6)
+                    assert np.all(err <= bound)
+
+
+def test_quantize_blocks_without_hadamard_is_torch_cast_of_scaled():
+    x = torch.randn(1, 2, 256, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    xf = x.double().numpy()
+    codes, scales = oracle.quantize_blocks(xf, False)
+    for j in range(2):
+        blk = xf[:, :, j * 128:(j + 1) * 128]
+        s = np.abs(blk).max(axis=(2, 3)) / 448.0
+        ref = torch.from_numpy(blk / s[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(codes[:, :, j * 128:(j + 1) * 128], ref)
+
+
+# ---------------------------------------------------------------------------
+# FP8 attention emulation
+def _exact_codes(shape):
+    """Random E4M3 codes whose every 128-row block holds a +-448 element, so
+    the block scale is exactly 1 and dequantisation returns the code values."""
+    c = rng.integers(0, 0x7F, size=shape).astype(np.uint8)
+    c = np.where(c >= 0x78, c - 0x40, c).astype(np.uint8)     # keep magnitudes moderate
+    c |= (rng.random(shape) < 0.5).astype(np.uint8) << 7
+    for j in range(0, shape[2], 128):
+        c[:, :, j, 0] = 0x7E
+    return c
+
+
+def test_attention_fp8_without_p_quant_is_plain_attention():
+    shape = (1, 2, 200, 128)
+    q8, k8, v8 = _exact_codes(shape), _exact_codes(shape), _exact_codes(shape)
+    ones = np.ones((1, 2, 2), dtype=np.float32)
+    o, lse = oracle.attention_fp8(q8, k8, v8, ones, ones, ones, 1e-3, True, quantize_p=False)
+    o_ref, lse_ref = attention(oracle.e4m3_decode(q8), oracle.e4m3_decode(k8), oracle.e4m3_decode(v8), 1e-3, True)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-12)
+
+
+def test_attention_fp8_p_quant_error_bound():
+    # each quantised p is within 2^-4 relative (normals) or 2^-18 absolute (subnormals of 256 p)
+    shape = (1, 1, 256, 128)
+    q, k, v = (rng.standard_normal(shape) for _ in range(3))
+    q8, qs = oracle.quantize_blocks(q, False)
+    k8, ks = oracle.quantize_blocks(k, False)
+    v8, vs = oracle.quantize_blocks(v, False)
+    o_q, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, False, quantize_p=True)
+    o_n, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, False, quantize_p=False)
+    vmax = np.abs(oracle.dequantize_blocks(v8, vs)).max()
+    assert np.abs(o_q - o_n).max() <= (2.0 ** -4 + 256 * 2.0 ** -18) * vmax
+    assert np.abs(o_q - o_n).max() > 0
+
+
+def test_fp8_incoherent_processing_helps_at_1k_tokens():
+    # outlier inputs as in the FP8 workload, at a short sequence where the
+    # Hadamard arm is expected to have the lower error
+    N, d, H = 1024, 128, 4
+    g = torch.Generator().manual_seed(99)
+    q, k, v = (torch.randn(1, H, N, d, generator=g) for _ in range(3))
+    for t in (q, k):
+        m = torch.rand(t.shape, generator=g) < 0.001
+        t[m] = 20.0 * (torch.randint(0, 2, t.shape, generator=g)[m] * 2.0 - 1.0)
+    q, k, v = (t.to(torch.bfloat16).double().numpy() for t in (q, k, v))
+    scale = d ** -0.5
+    o_ref, _ = attention(q, k, v, scale, True)
+    errs = {}
+    for had in (False, True):
+        q8, qs = oracle.quantize_blocks(q, had)
+        k8, ks = oracle.quantize_blocks(k, had)
+        v8, vs = oracle.quantize_blocks(v, False)
+        o, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, scale, True)
+        errs[had] = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
+    assert 0.02 < errs[True] < errs[False] < 0.1, errs
