@@ -1,0 +1,125 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention forward library (libfa.so), gfx950.
+ *
+ * What is computed.  Per (batch b, head h) the library returns
+ *     O = softmax(scale * Q K^T + mask) V      and      LSE_i = ln sum_j exp(scale * q_i . k_j)
+ * (the sum over the keys row i may see), computed tile by tile with a running
+ * (online) softmax so that the N x N score matrix never exists in memory:
+ *   - "Flash Attention" glossary page (news.hamidun.com), second paragraph:
+ *     tiles small enough for on-chip memory, a numerically stable online
+ *     softmax accumulating partial results, the full matrix never written to
+ *     HBM, memory linear in N;
+ *   - "FlashAttention-3 (PT)", section "FlashAttention e FlashAttention-2":
+ *     tiling in on-chip SRAM and fusion of the matmuls and softmax into one
+ *     kernel, no intermediate results in global memory.
+ * The FP8 variant follows "FlashAttention-3 (PT)", section "Inovacoes
+ * tecnicas", item 3: Q and K are multiplied by an orthogonal (Hadamard)
+ * matrix before FP8 quantisation ("incoherent processing"), which leaves
+ * Q K^T unchanged.
+ *
+ * Conventions shared by every entry point.
+ *   Layout:   Q, K, V, O are [B, H, N, d] contiguous row-major (d fastest);
+ *             LSE is [B, H, N] float32; FP8 tensors are E4M3 bytes (OCP "fn"
+ *             variant: bias 7, max 448, no infinities) in the same layout;
+ *             FP8 block scales are [B, H, ceil(N/128)] float32, one per
+ *             (b, h, block of 128 consecutive tokens).
+ *   Causal:   square, top-left aligned: key j is visible to query i iff j <= i.
+ *   Pointers: all tensor pointers are DEVICE pointers owned by the caller.
+ *             Inputs are only read.  Outputs must not overlap inputs or each
+ *             other (identical pointers are rejected; partial overlap is the
+ *             caller's error and is not detected).
+ *   Stream:   `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *             enqueued asynchronously on it; the call never synchronises.
+ *             Results are valid once the caller has synchronised that stream.
+ *   Memory:   the library allocates nothing and keeps no mutable global state;
+ *             concurrent calls from several host threads are safe.
+ *   Errors:   arguments are checked before any HIP call.  On a negative status
+ *             nothing has been enqueued and the outputs are untouched, except
+ *             FA_ERR_LAUNCH, which reports a failed kernel launch.  Device
+ *             faults surface at the caller's next synchronisation.  NaN or Inf
+ *             in the inputs is not an error; it propagates to the rows it
+ *             reaches.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype {
+  FA_F32 = 0,       /* float32 tensors */
+  FA_BF16 = 1,      /* bfloat16 tensors */
+  FA_FP8_E4M3 = 2   /* E4M3 bytes (only through fa_fwd_fp8 / fa_hadamard_fp8_quant) */
+};
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,         /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,        /* B, H or N < 1, or a size overflows the 64-bit/grid limits */
+  FA_ERR_DTYPE = -3,        /* unknown dtype code, or FA_FP8_E4M3 passed to fa_fwd */
+  FA_ERR_UNSUPPORTED = -4,  /* head dimension not supported for this dtype/entry point */
+  FA_ERR_LAUNCH = -5,       /* the kernel launch failed (hipGetLastError) */
+  FA_ERR_ARG = -6           /* non-finite scale, flag not 0/1, or an output aliasing an input */
+};
+
+/*
+ * fa_fwd -- fused attention forward in float32 or bfloat16.
+ *   q, k, v : [B,H,N,d] inputs, dtype `dtype` (FA_F32 or FA_BF16).
+ *   o       : [B,H,N,d] output, same dtype as the inputs.
+ *   lse     : [B,H,N] float32 output, natural-log units of the scaled scores.
+ *   B, H, N : batch, heads, tokens (>= 1 each); d : head dimension, 64 or 128.
+ *   scale   : any finite float multiplying Q K^T (usually 1/sqrt(d)).
+ *   causal  : 0 or 1.
+ * bf16 runs the products on bf16 matrix cores with float32 accumulation and a
+ * float32 softmax; f32 runs entirely in float32 arithmetic.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/*
+ * fa_fwd_fp8 -- fused attention forward on per-block-scaled E4M3 operands.
+ *   q8, k8, v8        : [B,H,N,128] E4M3 bytes (typically from fa_hadamard_fp8_quant,
+ *                       with the Hadamard matrix applied to q and k and not to v).
+ *   q_scale, k_scale,
+ *   v_scale           : [B,H,ceil(N/128)] float32 block scales; element value = code * scale.
+ *   o                 : [B,H,N,128] bfloat16 output;  lse : [B,H,N] float32 output.
+ *   d                 : must be 128.
+ * S = scale * (q8 k8^T) runs on FP8 matrix cores with the two block scales
+ * folded into the softmax exponent; P is quantised to E4M3 as 256*p (p <= 1),
+ * multiplied with v8 on FP8 matrix cores, and the v scale and 1/256 are undone
+ * in float32.  (The dtype argument of fa_fwd has no room for the block scales,
+ * hence a separate entry point.)
+ */
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+               const float* q_scale, const float* k_scale, const float* v_scale,
+               void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_hadamard_fp8_quant -- incoherent processing and per-block FP8 quantisation.
+ *   x        : [B,H,N,d] input, in_dtype FA_BF16 or FA_F32.
+ *   x8       : [B,H,N,d] E4M3 output bytes.
+ *   scales   : [B,H,ceil(N/128)] float32 output block scales.
+ *   hadamard : 1 = first multiply every row by the Sylvester Hadamard matrix of
+ *              order d divided by sqrt(d) (d must be 128); 0 = quantise x as is
+ *              (any d in {64,128}).
+ * Per block of 128 tokens (fewer in the last block): amax = max |y| over the
+ * block, s = amax / 448 (s = 1 when amax = 0), code = E4M3 round-to-nearest-even
+ * of y / s.  The transform is computed exactly (float64 butterflies), so the
+ * codes do not depend on summation order.
+ */
+int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scales,
+                          int B, int H, int N, int d, int hadamard, void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

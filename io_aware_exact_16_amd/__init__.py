@@ -1,0 +1,12 @@
+"""Fused exact attention forward for MI355X (gfx950).
+
+The computation lives in libfa.so (C ABI in include/fa.h, HIP kernels in
+csrc/); ``binding`` exposes its entry points to Python with torch tensors for
+device memory and streams.  ``workloads`` draws the seeded synthetic inputs.
+Importing the package loads nothing; the library is loaded on first use.
+"""
+from .binding import (FaError, attention, attention_fp8, fa_fwd, fa_fwd_fp8, fa_hadamard_fp8_quant,
+                      fa_status_string, library_path, load, quant_fp8)
+
+__all__ = ["FaError", "attention", "attention_fp8", "fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant",
+           "fa_status_string", "library_path", "load", "quant_fp8"]

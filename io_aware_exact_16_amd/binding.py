@@ -1,0 +1,166 @@
+"""Thin Python binding of libfa.so (include/fa.h), argument marshalling only.
+
+Every function here checks the torch tensors it is given, passes their device
+pointers, sizes and the current HIP stream to the C entry point of the same
+name, and raises on a negative status.  No step of the computation runs in
+Python or in torch: torch only allocates device memory and supplies the
+stream.  If libfa.so is missing or cannot be loaded the functions raise; there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
+                -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG"}
+EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_status_string")
+BLOCK = 128   # tokens per FP8 scaling block
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)}: {fa_status_string(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m io_aware_exact_16_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, P]
+    lib.fa_fwd.restype = I
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
+    lib.fa_fwd_fp8.restype = I
+    lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    lib.fa_hadamard_fp8_quant.restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(fn, status):
+    if status != FA_OK:
+        raise FaError(fn, status)
+
+
+def _dev4(name, t, dtype, shape=None):
+    if not (t.is_cuda and t.is_contiguous() and t.dtype == dtype and t.dim() == 4):
+        raise ValueError(f"{name}: need a contiguous 4-d {dtype} CUDA tensor, got {t.dtype} {tuple(t.shape)}"
+                         f" cuda={t.is_cuda} contiguous={t.is_contiguous()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one to one
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool) -> None:
+    """O, LSE <- attention(q, k, v); q/k/v/o [B,H,N,d] fp32 or bf16, lse [B,H,N] fp32."""
+    dtype = q.dtype
+    code = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(dtype)
+    if code is None:
+        raise ValueError(f"fa_fwd: unsupported dtype {dtype}")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _dev4(name, t, dtype, (B, H, N, d))
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("fa_fwd: lse must be a contiguous float32 CUDA tensor [B,H,N]")
+    st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                       code, _stream(q))
+    _check("fa_fwd", st)
+
+
+def fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, scale: float, causal: bool) -> None:
+    """O (bf16), LSE <- attention on per-block-scaled E4M3 operands (uint8 tensors)."""
+    B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _dev4(name, t, torch.uint8, (B, H, N, d))
+    _dev4("o", o, torch.bfloat16, (B, H, N, d))
+    nb = -(-N // BLOCK)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and tuple(t.shape) == (B, H, nb)):
+            raise ValueError(f"fa_fwd_fp8: {name} must be a contiguous float32 CUDA tensor [B,H,{nb}]")
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("fa_fwd_fp8: lse must be a contiguous float32 CUDA tensor [B,H,N]")
+    st = load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o),
+                           _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), _stream(q8))
+    _check("fa_fwd_fp8", st)
+
+
+def fa_hadamard_fp8_quant(x, x8, scales, hadamard: bool) -> None:
+    """x8 (uint8 E4M3), scales [B,H,ceil(N/128)] <- per-block quantisation of x
+    (bf16 or fp32), after the normalised Hadamard transform when ``hadamard``."""
+    code = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(x.dtype)
+    if code is None:
+        raise ValueError(f"fa_hadamard_fp8_quant: unsupported dtype {x.dtype}")
+    B, H, N, d = x.shape
+    _dev4("x", x, x.dtype)
+    _dev4("x8", x8, torch.uint8, (B, H, N, d))
+    nb = -(-N // BLOCK)
+    if not (scales.is_cuda and scales.is_contiguous() and scales.dtype == torch.float32
+            and tuple(scales.shape) == (B, H, nb)):
+        raise ValueError(f"fa_hadamard_fp8_quant: scales must be a contiguous float32 CUDA tensor [B,H,{nb}]")
+    st = load().fa_hadamard_fp8_quant(_ptr(x), code, _ptr(x8), _ptr(scales), B, H, N, d, int(bool(hadamard)),
+                                      _stream(x))
+    _check("fa_hadamard_fp8_quant", st)
+
+
+# ---------------------------------------------------------------------------
+# allocating conveniences (torch allocates the outputs, the library computes)
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """Return (o, lse) for q, k, v [B,H,N,d] (bf16 or fp32, on the GPU)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def quant_fp8(x, hadamard: bool = True):
+    """Return (x8, scales): E4M3 codes as uint8 [B,H,N,d] and float32 block scales."""
+    B, H, N, d = x.shape
+    x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, -(-N // BLOCK)), dtype=torch.float32, device=x.device)
+    fa_hadamard_fp8_quant(x, x8, scales, hadamard)
+    return x8, scales
+
+
+def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None):
+    """Return (o bf16, lse fp32) for E4M3 operands and their block scales."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q8.shape[-1])
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, scale, causal)
+    return o, lse

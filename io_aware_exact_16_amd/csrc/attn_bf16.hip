@@ -1,0 +1,292 @@
+// Fused exact attention forward, bf16 in / bf16 out, float32 softmax, gfx950.
+//
+// Method ("Flash Attention" glossary page, second paragraph; "FlashAttention-3
+// (PT)", section "FlashAttention e FlashAttention-2"): one kernel walks the
+// key/value sequence tile by tile, keeps a running row maximum and row sum
+// (online softmax), rescales the partial output when the maximum grows, and
+// never writes the score matrix to HBM.  The work is split over query blocks,
+// heads and batches (FlashAttention-2's parallelism over the sequence), and
+// the 1/l normalisation is deferred to the end (its fewer non-matmul FLOPs).
+//
+// gfx950 mapping (the Hopper design on the pages -- WGMMA, TMA, warp
+// specialisation -- is prior art, not reproduced):
+//  * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
+//    query rows; key/value tiles of 64 rows stream through LDS, double
+//    buffered so the next tile's global loads overlap this tile's math;
+//  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
+//    with the 32x32 accumulator layout each lane then holds 16 keys of ONE
+//    query, so the row max / row sum are in-register reductions plus a single
+//    exchange between the two half-waves (v_permlane32_swap), and the running
+//    statistics and the output rescale are per-lane scalars;
+//  * the output is accumulated transposed too, O^T += V^T P^T: the score
+//    accumulator registers, rounded to bf16, are directly the B operand, and
+//    V^T comes out of the row-major LDS tile through ds_read_b64_tr_b16;
+//  * Q^T stays in registers for the whole key loop;
+//  * exp2 with the scale folded into one FMA (c = scale * log2 e);
+//  * the reference maximum is only moved when a tile's maximum exceeds it by
+//    more than 2^8 (in the exp2 domain): p = exp2(c s - m) <= 256 stays exact in
+//    float32 and bf16 range, the final O / l and LSE are unchanged, and the
+//    O rescale (D/2 multiplies per lane) is skipped on almost every tile.
+//
+// Register-level layouts (lane l of 64, h = l / 32; verified on gfx950):
+//   32x32x16 bf16 MFMA: A[i][k] in lane (i + 32 * (k / 8)), element k % 8;
+//   B[k][j] in lane (j + 32 * (k / 8)), element k % 8; C[i][j] in lane
+//   (j + 32 * ((i / 4) % 2)), register 4 * (i / 8) + i % 4.
+//   ds_read_b64_tr_b16: within each 16-lane group, lane 4r + c names the 4
+//   elements at [r][4c..4c+3] of a 4 x 16 tile; lane j receives column j.
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int BR = 128;   // query rows per workgroup
+constexpr int BC = 64;    // key rows per tile
+constexpr int NT = 256;   // threads per workgroup
+constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the allowed growth of p
+
+// Position (in 16-byte chunks) of chunk `ch` of tile row `row` in LDS.  The
+// XOR swizzle makes both read patterns of the kernel conflict-free: 16 lanes
+// reading 16 B from 16 different rows (K operand), and 32 lanes reading
+// 8 B from 4 rows x 4 chunks (transposed V operand).
+template <int D>
+__device__ __forceinline__ int lds_chunk(int row, int ch) {
+  const int s = (D == 128) ? (((row & 3) << 2) | ((row >> 2) & 3))
+                           : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  return row * (D / 8) + (ch ^ s);
+}
+
+// Row of a 32-key block that A-operand row m must hold so that, in the
+// accumulator layout, the 8 registers r = 0..7 (8..15) of half-wave h hold keys
+// 8h + r (16 + 8h + r - 8): consecutive keys, ready to be the B operand of P V.
+// It swaps bits 2 and 3 of m.
+__device__ __forceinline__ int key_of_arow(int m) {
+  return (m & 0x13) | ((m >> 1) & 0x4) | ((m << 1) & 0x8);
+}
+
+__device__ __forceinline__ float wave_halves_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float wave_halves_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT) void attn_fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c,
+    uint32_t qflip) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE_CHUNKS = BC * CPR;      // chunks per K (or V) tile
+  constexpr int LD = TILE_CHUNKS / NT;       // chunks each thread moves per tile and tensor
+  __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
+
+  const int L = xcd_logical_id(blockIdx.x, total);
+  const int bh = L / nqb;
+  int qb = L - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;             // longest query blocks first
+  const int q0 = qb * BR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int qw = q0 + 32 * wave;             // first query row of this wave
+  const size_t hoff = (size_t)bh * N * D;
+
+  // Q^T as the B operand: lane holds query qw + l32, dims 16*dc + 8*half + 0..7
+  bf16x8 qf[D / 16];
+  {
+    const int qi = qw + l32;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (qi < N) u = *reinterpret_cast<const uint4*>(Q + hoff + (size_t)qi * D + 16 * dc + 8 * half);
+      u.x ^= qflip; u.y ^= qflip; u.z ^= qflip; u.w ^= qflip;
+      qf[dc] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  uint4 kreg[LD], vreg[LD];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int id = i * NT + tid, row = id / CPR, ch = id % CPR, key = j0 + row;
+      if (key < N) {
+        kreg[i] = *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + 8 * ch);
+        vreg[i] = *reinterpret_cast<const uint4*>(V + hoff + (size_t)key * D + 8 * ch);
+      } else {
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int id = i * NT + tid, row = id / CPR, ch = id % CPR;
+      smem[buf][0][lds_chunk<D>(row, ch)] = kreg[i];
+      smem[buf][1][lds_chunk<D>(row, ch)] = vreg[i];
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m2 = -INFINITY;   // reference maximum, exp2 domain (c * raw score)
+  float lsum = 0.0f;      // this half-wave's share of the row sum
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BC;
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) load_tile(j0 + BC);
+
+    const bool active = !CAUSAL || j0 <= qw + 31;
+    if (active) {
+      const uint4* Ks = smem[t & 1][0];
+      const uint4* Vs = smem[t & 1][1];
+
+      // S^T = K Q^T for the 64 keys of the tile, two 32-key blocks
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+        const int row = 32 * kb + key_of_arow(l32);
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, Ks[lds_chunk<D>(row, 2 * dc + half)]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
+        }
+      }
+
+      // mask: keys past the end, and keys after the query on the diagonal
+      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
+      if (need_mask) {
+        const int qi = qw + l32;
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
+            if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+          }
+      }
+
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+      tmax = wave_halves_max(tmax);
+      const float tm2 = tmax * c;
+      if (__any(tm2 > m2 + RESCALE_THRESHOLD)) {
+        const float mnew = fmaxf(m2, tm2);
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        lsum *= alpha;
+        m2 = mnew;
+      }
+
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sv = s[kb][r];
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -m2));
+          if (need_mask && sv == -INFINITY) p = 0.0f;
+          s[kb][r] = p;
+          rs += p;
+        }
+      lsum += rs;
+
+      // O^T += V^T P^T, 16 keys per MFMA
+      const int b16 = lane >> 4, j16 = lane & 15;
+      const char* vbytes = reinterpret_cast<const char*>(Vs);
+#pragma unroll
+      for (int kc = 0; kc < BC / 16; ++kc) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kc >> 1][8 * (kc & 1) + e];
+        const int key = 16 * kc + 8 * (b16 >> 1) + (j16 >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int dcol = 32 * db + 16 * (b16 & 1) + 4 * (j16 & 3);
+          const char* p0 = vbytes + 16 * lds_chunk<D>(key, dcol >> 3) + 2 * (dcol & 7);
+          const char* p1 = vbytes + 16 * lds_chunk<D>(key + 4, dcol >> 3) + 2 * (dcol & 7);
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(p0));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(p1));
+          const short __attribute__((__vector_size__(8 * sizeof(short)))) vv = {
+              v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb, acc[db],
+                                                             0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // epilogue: O = O / l, LSE = ln 2 * (m2 + log2 l)
+  const float ltot = wave_halves_sum(lsum);
+  const int qi = qw + l32;
+  if (qi < N) {
+    const float inv = 1.0f / ltot;
+    uint16_t* orow = O + hoff + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * half;
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+        bf16x4 w = {(__bf16)(acc[db][4 * a + 0] * inv), (__bf16)(acc[db][4 * a + 1] * inv),
+                    (__bf16)(acc[db][4 * a + 2] * inv), (__bf16)(acc[db][4 * a + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(orow + d0) = w;
+      }
+    if (half == 0) LSE[(size_t)bh * N + qi] = (m2 + __log2f(ltot)) * 0.69314718055994531f;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                  float scale, hipStream_t stream) {
+  const int nqb = (N + BR - 1) / BR;
+  const int total = nqb * H * B;
+  const float c = (float)((double)__builtin_fabsf(scale) * 1.4426950408889634);
+  const uint32_t qflip = scale < 0.0f ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(NT), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, nqb, total, c, qflip);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int N, int d, float scale, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
+                              : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+  return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
+                : launch<64, false>(q, k, v, o, lse, B, H, N, scale, stream);
+}
+
+}  // namespace fa

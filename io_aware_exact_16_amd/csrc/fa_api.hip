@@ -1,0 +1,85 @@
+// C entry points of libfa.so: argument checks, kernel-instance dispatch, launch
+// on the caller's stream.  Declared and documented in include/fa.h.
+#include <math.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr long long kMaxGrid = 2147483647LL;
+
+bool sizes_ok(int B, int H, int N, int d, int rows_per_block) {
+  if (B < 1 || H < 1 || N < 1) return false;
+  const long long heads = (long long)B * H;
+  const long long blocks = heads * ((N + (long long)rows_per_block - 1) / rows_per_block);
+  if (blocks > kMaxGrid) return false;
+  // element offsets are computed in 64 bits; keep the tensor far from overflow
+  const long double elems = (long double)heads * N * d;
+  return elems < 9.0e18L;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;   // FP8 goes through fa_fwd_fp8
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, N, d, 64)) return FA_ERR_SHAPE;
+  if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k || (const void*)lse == v ||
+      (void*)lse == o)
+    return FA_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16) return launch_status(fa::launch_attn_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, s));
+  return launch_status(fa::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, N, d,
+                                           scale, causal, s));
+}
+
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, N, d, 64)) return FA_ERR_SHAPE;
+  if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  const void* ins[6] = {q8, k8, v8, q_scale, k_scale, v_scale};
+  for (const void* p : ins)
+    if (p == o || p == (const void*)lse) return FA_ERR_ARG;
+  if ((void*)lse == o) return FA_ERR_ARG;
+  return launch_status(fa::launch_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, scale, causal,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scales, int B, int H, int N, int d,
+                          int hadamard, void* stream) {
+  if (!x || !x8 || !scales) return FA_ERR_NULL;
+  if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_DTYPE;
+  if (hadamard != 0 && hadamard != 1) return FA_ERR_ARG;
+  if (d != 128 && !(d == 64 && !hadamard)) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, N, d, 128)) return FA_ERR_SHAPE;
+  if ((const void*)x8 == x || (const void*)scales == x || (void*)scales == (void*)x8) return FA_ERR_ARG;
+  return launch_status(fa::launch_hadamard_fp8_quant(x, in_dtype == FA_BF16, x8, scales, B, H, N, d, hadamard != 0,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N below 1, or the sizes exceed the supported range";
+    case FA_ERR_DTYPE: return "unknown or unsupported dtype for this entry point";
+    case FA_ERR_UNSUPPORTED: return "head dimension not supported for this entry point";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ARG: return "invalid argument: non-finite scale, flag not 0/1, or output aliasing an input";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal declarations shared by the HIP translation units of libfa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Shapes are validated by the C entry points before these are called.
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
+
+hipError_t launch_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           const float* qs, const float* ks, const float* vs, void* o, float* lse,
+                           int B, int H, int N, float scale, bool causal, hipStream_t stream);
+
+hipError_t launch_hadamard_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8, float* scales,
+                                     int B, int H, int N, int d, bool hadamard, hipStream_t stream);
+
+// Workgroups are handed to the 8 XCDs round-robin by workgroup id.  This maps
+// the hardware id to a logical id so that each XCD receives one contiguous
+// range of logical ids (neighbouring query blocks of the same heads share the
+// XCD's L2).  A bijection on [0, total) for any total.
+__device__ __forceinline__ int xcd_logical_id(int lin, int total) {
+  const int xcd = lin & 7, idx = lin >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace fa

@@ -1,0 +1,177 @@
+"""GPU parity of the fused attention kernels (bf16 and fp32) against the fp64
+oracle, on seeded inputs: edge shapes, every workload at full size (whole
+output where the oracle is fast, sampled rows otherwise), the special cases the
+method has, and the API contract (no allocation, determinism, streams)."""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_16_amd as fa
+import oracle
+from io_aware_exact_16_amd.workloads import WORKLOADS, custom, make_qkv
+
+from gpu_helpers import compare, compare_sampled, f64, log, run_attention, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(w, kind):
+    q, k, v = make_qkv(w)
+    log(f"[{w.name}] B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    o, lse = run_attention(q, k, v, w.causal, w.scale)
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), w.scale, w.causal)
+    return compare(o, lse, o_ref, lse_ref, kind)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 1000])
+def test_bf16_edge_shapes(gpu, N, d, causal):
+    _check_full(custom(1, 2, N, d, causal, "bf16", seed=N * 7 + d), "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 5, 64, 100, 128, 300])
+def test_f32_edge_shapes(gpu, N, d, causal):
+    _check_full(custom(1, 2, N, d, causal, "f32", seed=N * 5 + d), "f32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_several_tiles_ragged(gpu, d, causal):
+    # 3000 = 23 * 128 + 56: many query blocks and key tiles plus a ragged tail
+    _check_full(custom(2, 3, 3000, d, causal, "bf16", seed=3000 + d), "bf16")
+
+
+def test_workload_f32_tiny(gpu):
+    _check_full(WORKLOADS["f32_tiny"], "f32")
+
+
+def test_workload_bf16_causal_2k_full(gpu):
+    e = _check_full(WORKLOADS["bf16_causal_2k"], "bf16")
+    log(f"  max|dO|={e[0]:.3g} max rel dLSE={e[1]:.3g}")
+
+
+@pytest.mark.parametrize("name", ["bf16_d64_4k", "bf16_causal_8k", "bf16_causal_32k"])
+def test_workload_sampled_rows(gpu, name):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    log(f"[{name}] B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} (sampled rows)")
+    o, lse = run_attention(q, k, v, w.causal, w.scale)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    e = compare_sampled(q, k, v, o, lse, w.causal, w.scale, "bf16", heads, sample_rows(w.N, 96, 11))
+    # properties that hold for every row: finite, and |O| within the range of V
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.abs(o).max() <= np.abs(f64(v)).max() * (1 + 2 ** -7)
+    log(f"  max|dO|={e[0]:.3g} max rel dLSE={e[1]:.3g}")
+
+
+def test_long_context_allocates_nothing(gpu):
+    w = WORKLOADS["bf16_causal_32k"]
+    q, k, v = to_dev(*make_qkv(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)        # first call may load code objects
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0
+    assert free1 == free0, f"device free memory changed by {free0 - free1} bytes during the call"
+
+
+# ---------------------------------------------------------------------------
+# special cases of the method, through the GPU path
+def _bf16(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_v(gpu, causal):
+    g = torch.Generator().manual_seed(5)
+    N, d = 300, 128
+    q = torch.randn(1, 2, N, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 2, 1, d, generator=g).expand(1, 2, N, d).contiguous().to(torch.bfloat16)
+    v = torch.randn(1, 2, N, d, generator=g).to(torch.bfloat16)
+    o, lse = run_attention(q, k, v, causal, d ** -0.5)
+    vn = f64(v)
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = np.cumsum(vn, axis=2) / cnt[:, None] if causal else np.broadcast_to(vn.mean(axis=2, keepdims=True), vn.shape)
+    assert np.abs(o - mean).max() <= 2e-2
+    ref_lse = d ** -0.5 * np.einsum("bhnd,bhd->bhn", f64(q), f64(k)[:, :, 0]) + np.log(cnt)
+    assert (np.abs(lse - ref_lse) / np.maximum(1, np.abs(ref_lse))).max() <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_token_returns_v(gpu, d):
+    g = torch.Generator().manual_seed(6)
+    q, k, v = (torch.randn(3, 4, 1, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    for causal in (False, True):
+        o, lse = run_attention(q, k, v, causal, 0.3)
+        np.testing.assert_array_equal(o, f64(v))
+        np.testing.assert_allclose(lse, 0.3 * np.einsum("bhnd,bhnd->bhn", f64(q), f64(k)), rtol=1e-5, atol=1e-5)
+
+
+def test_causal_first_row_is_v0(gpu):
+    q, k, v = make_qkv(custom(2, 3, 777, 128, True, "bf16", seed=8))
+    o, lse = run_attention(q, k, v, True, 128 ** -0.5)
+    np.testing.assert_array_equal(o[:, :, 0], f64(v)[:, :, 0])
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
+def test_unusual_scales(gpu, scale):
+    # scale 0 is uniform attention; a negative scale flips the scores; a large one sharpens them
+    for causal in (False, True):
+        q, k, v = make_qkv(custom(1, 2, 333, 64, causal, "bf16", seed=9))
+        o, lse = run_attention(q, k, v, causal, scale)
+        o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), scale, causal)
+        compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_incoherent_inputs_match_oracle(gpu):
+    # Q H and K H (normalised Hadamard) as inputs: same parity bar
+    q, k, v = make_qkv(custom(1, 2, 1000, 128, True, "bf16", seed=10, outlier_frac=0.001))
+    h = torch.from_numpy(oracle.orthonormal_hadamard(128)).float()
+    qh, kh = (q.float() @ h).to(torch.bfloat16), (k.float() @ h).to(torch.bfloat16)
+    o, lse = run_attention(qh, kh, v, True, 128 ** -0.5)
+    o_ref, lse_ref = oracle.attention(f64(qh), f64(kh), f64(v), 128 ** -0.5, True)
+    compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# API contract
+def test_deterministic(gpu):
+    q, k, v = to_dev(*make_qkv(custom(2, 4, 2500, 128, True, "bf16", seed=12)))
+    o1, l1 = fa.attention(q, k, v, causal=True)
+    o2, l2 = fa.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_runs_on_the_callers_stream(gpu):
+    q, k, v = to_dev(*make_qkv(custom(1, 2, 1024, 128, False, "bf16", seed=13)))
+    ref_o, ref_l = fa.attention(q, k, v)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = fa.attention(q, k, v)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_error_status_with_device_tensors(gpu):
+    q = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.attention(q, q.clone(), q.clone())
+    assert e.value.status == -4
+    q = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((1, 1, 16), 7.0, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(q, q, q, o, lse, float("nan"), False)
+    assert e.value.status == -6
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0) and torch.all(lse == 7.0)      # outputs untouched on error

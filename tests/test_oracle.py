@@ -306,15 +306,43 @@ def test_quantize_blocks_properties():
                     assert np.all(err <= bound)
 
 
-def test_quantize_blocks_without_hadamard_is_torch_cast_of_scaled():
-    x = torch.randn(1, 2, 256, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
-    xf = x.double().numpy()
-    codes, scales = oracle.quantize_blocks(xf, False)
+@pytest.mark.parametrize("outliers", [False, True])
+def test_quantize_blocks_without_hadamard_is_torch_cast_of_scaled(outliers):
+    # torch computes the same float32 quotient x * (448 / amax) and casts it
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(1, 2, 256, 128, generator=g)
+    if outliers:
+        m = torch.rand(x.shape, generator=g) < 0.001
+        x[m] = 20.0
+    x = x.to(torch.bfloat16).float()
+    codes, scales = oracle.quantize_blocks(x.double().numpy(), False)
     for j in range(2):
-        blk = xf[:, :, j * 128:(j + 1) * 128]
-        s = np.abs(blk).max(axis=(2, 3)) / 448.0
-        ref = torch.from_numpy(blk / s[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        blk = x[:, :, j * 128:(j + 1) * 128]
+        amax = blk.abs().amax(dim=(2, 3), keepdim=True)
+        ref = (blk * (448.0 / amax)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         np.testing.assert_array_equal(codes[:, :, j * 128:(j + 1) * 128], ref)
+        np.testing.assert_array_equal(scales[:, :, j], (amax[:, :, 0, 0].double() / 448.0).float().numpy())
+
+
+def test_quantize_exact_tie_goes_to_even():
+    # a block with amax 20: x = 0.9375 scales to exactly 21, halfway between 20 and 22
+    x = np.zeros((1, 1, 128, 64))
+    x[0, 0, 0, 0], x[0, 0, 5, 7], x[0, 0, 9, 1] = 20.0, 0.9375, -0.9375
+    codes, scales = oracle.quantize_blocks(x, False)
+    assert oracle.e4m3_decode(codes[0, 0, 5, 7]) == 20.0 and oracle.e4m3_decode(codes[0, 0, 9, 1]) == -20.0
+    assert codes[0, 0, 0, 0] == 0x7E and codes[0, 0, 1, 1] == 0x00
+    assert scales[0, 0, 0] == np.float32(20.0 / 448.0)
+
+
+def test_quantize_hadamard_scale_is_amax_of_orthonormal_transform():
+    x = rng.standard_normal((1, 2, 130, 128))
+    codes, scales = oracle.quantize_blocks(x, True)
+    y = x @ oracle.orthonormal_hadamard(128)
+    for j, sl in enumerate((slice(0, 128), slice(128, 130))):
+        s = np.abs(y[:, :, sl]).max(axis=(2, 3)) / 448.0
+        np.testing.assert_allclose(scales[:, :, j], s, rtol=2.0 ** -23)
+    deq = oracle.dequantize_blocks(codes, scales)
+    assert np.abs(deq - y).max() <= np.abs(y).max() * 2.0 ** -4
 
 
 # ---------------------------------------------------------------------------
