@@ -26,7 +26,15 @@ Readings where the pages are silent:
   - scaling is per block: one scale per (batch, head, block of 128 tokens),
     over all d coordinates; s = amax / 448, or s = 1 when the block is all
     zero; the last block covers the remaining rows only; code = E4M3(y / s);
-    the scale is stored as float32 and dequantisation is code * s;
+    the scale is stored as float32 (s rounded once from float64) and
+    dequantisation is code * s;
+  - the rounding decision y / s -> code is taken in float32, the precision of
+    the quantiser kernel: with y_u = x H (the unnormalised +-1 matrix, exact in
+    float64 for these inputs) and A = max |y_u| over the block, the 1/sqrt(d)
+    cancels and y / s = 448 y_u / A, formed as RN32(RN32(y_u) * RN32(448 /
+    RN32(A))) (then + 0, so a zero quotient is +0); exact E4M3 ties are common
+    (for example y_u = 0.9375 in a block with amax 20 gives exactly 21), so
+    both sides must round the same float32 quotient;
   - V is quantised per block the same way, without the Hadamard matrix;
   - inside attention P is quantised as E4M3(256 p) / 256 with p = exp(S - m)
     relative to the row maximum; the row sum l uses the unquantised p.
@@ -92,16 +100,20 @@ def quantize_blocks(x, hadamard: bool, block: int = BLOCK):
     [B,H,ceil(N/block)])."""
     x = np.asarray(x, dtype=np.float64)
     B, H, N, d = x.shape
-    y = x @ orthonormal_hadamard(d) if hadamard else x
+    yu = x @ sylvester_hadamard(d) if hadamard else x          # y = yu / sqrt(d)
+    norm = E4M3_MAX * np.sqrt(float(d)) if hadamard else E4M3_MAX
     nb = -(-N // block)
     codes = np.empty((B, H, N, d), dtype=np.uint8)
     scales = np.empty((B, H, nb), dtype=np.float32)
     for j in range(nb):
-        blk = y[:, :, j * block:(j + 1) * block, :]
-        amax = np.abs(blk).max(axis=(2, 3))
-        s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
-        codes[:, :, j * block:(j + 1) * block, :] = e4m3_encode(blk / s[:, :, None, None])
-        scales[:, :, j] = s.astype(np.float32)
+        blk = yu[:, :, j * block:(j + 1) * block, :]
+        amax_u = np.abs(blk).max(axis=(2, 3))                  # amax = amax_u / sqrt(d)
+        a32 = amax_u.astype(np.float32)
+        with np.errstate(divide="ignore"):
+            inv32 = np.where(a32 > 0, np.float32(E4M3_MAX) / a32, np.float32(0)).astype(np.float32)
+        q32 = blk.astype(np.float32) * inv32[:, :, None, None] + np.float32(0)
+        codes[:, :, j * block:(j + 1) * block, :] = e4m3_encode(q32)
+        scales[:, :, j] = np.where(amax_u > 0, amax_u / norm, 1.0).astype(np.float32)
     return codes, scales
 
 
