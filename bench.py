@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+that is already resident in HBM: for the bf16/fp32 workloads one fa_fwd call;
+for the FP8 workload the three Hadamard/FP8 quantiser calls (Q and K with the
+transform, V without) followed by fa_fwd_fp8.  W untimed steps, then K timed
+steps bracketed by device synchronisation, timed with HIP events on the stream
+the kernels are launched on.  Prints ONE JSON line.
+
+Throughput counts attention FLOPs as 4*B*H*N^2*d (halved when causal) per
+step.  The roofline object reports the dominant kernel (the attention kernel)
+against the MI355X dense matrix peak of its input type; "traffic" is the HBM
+byte count per launch measured with hardware counters (profiles/traffic.json),
+or null when that kernel's source changed since the counters were taken.
+The cpu_baseline object times the float64 CPU oracle on a bounded sample of
+the same workload (whole heads) on this host.
+
+    python bench.py --copy-calibration    # a plain copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense, published
+KERNEL_SOURCE = {"bf16": "attn_bf16.hip", "fp8": "attn_fp8.hip", "f32": "attn_f32.hip"}
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(ROOT, "io_aware_exact_16_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, kernel_src: str):
+    """HBM bytes per launch from profiles/traffic.json, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_sha(kernel_src):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def copy_calibration(steps: int) -> None:
+    import torch
+    n = 256 * 1024 * 1024                      # 1 GiB of float32 read, 1 GiB written
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": steps}))
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the float64 oracle on whole heads of the workload until about budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle
+    qn = q.float().numpy().astype(np.float64)
+    kn = k.float().numpy().astype(np.float64)
+    vn = v.float().numpy().astype(np.float64)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_used = 0, 0.0
+    per_head = 4.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    for (b, h) in heads:
+        t0 = time.perf_counter()
+        oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], w.scale, w.causal)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": done * per_head / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) pairs, full rows, float64, {t_used:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return 0
+
+    import io_aware_exact_16_amd as fa
+    from io_aware_exact_16_amd.workloads import HEADLINE, WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    q, k, v = make_qkv(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    stream = torch.cuda.current_stream(dev)
+
+    if w.dtype == "fp8":
+        nb = -(-w.N // 128)
+        q8, k8, v8 = (torch.empty(qd.shape, dtype=torch.uint8, device=dev) for _ in range(3))
+        qs, ks, vs = (torch.empty((w.B, w.H, nb), dtype=torch.float32, device=dev) for _ in range(3))
+        o = torch.empty(qd.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+        def step(record=None):
+            fa.fa_hadamard_fp8_quant(qd, q8, qs, True)
+            fa.fa_hadamard_fp8_quant(kd, k8, ks, True)
+            fa.fa_hadamard_fp8_quant(vd, v8, vs, False)
+            if record is not None:
+                record[0].record(stream)
+            fa.fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, w.scale, w.causal)
+            if record is not None:
+                record[1].record(stream)
+    else:
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+        def step(record=None):
+            if record is not None:
+                record[0].record(stream)
+            fa.fa_fwd(qd, kd, vd, o, lse, w.scale, w.causal)
+            if record is not None:
+                record[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events around every attention launch on the launch stream
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(pairs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    kern_ms = [a.elapsed_time(b) for a, b in pairs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    ms_per_step = total_ms / args.steps
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    dtype = w.dtype
+    peak = PEAK_TFLOPS[dtype]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, KERNEL_SOURCE[dtype])}
+    eprint(f"[bench] {w.name}: step {ms_per_step:.4f} ms, attention kernel avg {kern_avg_ms:.4f} ms "
+           f"(min {min(kern_ms):.4f}), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} peak")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint("[bench] timing the CPU oracle on a sample of the workload ...")
+        cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
+        eprint(f"[bench] cpu_baseline: {cpu}")
+
+    line = {
+        "metric": "attention fwd TFLOPS (4*B*H*N^2*d, x1/2 causal) and % of MFMA peak, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[dtype], "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "input_dist": f"iid N(0,{w.std}^2)" + (f", {w.outlier_frac:.1%} coords = +-{w.outlier_value:g}"
+                                                         if w.outlier_frac else ""),
+                   "seed": w.seed},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
