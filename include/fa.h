@@ -58,7 +58,8 @@ enum fa_dtype {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,         /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,        /* B, H or N < 1, or a size overflows the 64-bit/grid limits */
+  FA_ERR_SHAPE = -2,        /* B, H or N < 1, or a size exceeds the limits: the grid, 64-bit offsets,
+                               and N * d * 4 < 2^32 (one head's K or V is addressed with 32-bit offsets) */
   FA_ERR_DTYPE = -3,        /* unknown dtype code, or FA_FP8_E4M3 passed to fa_fwd */
   FA_ERR_UNSUPPORTED = -4,  /* head dimension not supported for this dtype/entry point */
   FA_ERR_LAUNCH = -5,       /* the kernel launch failed (hipGetLastError) */

@@ -12,7 +12,11 @@
 // specialisation -- is prior art, not reproduced):
 //  * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
 //    query rows; key/value tiles of 64 rows stream through LDS, double
-//    buffered so the next tile's global loads overlap this tile's math;
+//    buffered so the next tile's loads overlap this tile's math; the loads go
+//    straight from HBM/L2 to LDS (buffer_load_dwordx4 ... lds: no staging
+//    registers; the buffer range check returns zeros past the last token);
+//  * at most 256 registers per lane, so two waves share each SIMD and the
+//    hardware overlaps one wave's softmax with the other's matrix ops;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //    with the 32x32 accumulator layout each lane then holds 16 keys of ONE
 //    query, so the row max / row sum are in-register reductions plus a single
@@ -53,10 +57,13 @@ constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the allowed growth of p
 // reading 16 B from 16 different rows (K operand), and 32 lanes reading
 // 8 B from 4 rows x 4 chunks (transposed V operand).
 template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return (D == 128) ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+template <int D>
 __device__ __forceinline__ int lds_chunk(int row, int ch) {
-  const int s = (D == 128) ? (((row & 3) << 2) | ((row >> 2) & 3))
-                           : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-  return row * (D / 8) + (ch ^ s);
+  return row * (D / 8) + (ch ^ swz<D>(row));
 }
 
 // Row of a 32-key block that A-operand row m must hold so that, in the
@@ -65,6 +72,15 @@ __device__ __forceinline__ int lds_chunk(int row, int ch) {
 // It swaps bits 2 and 3 of m.
 __device__ __forceinline__ int key_of_arow(int m) {
   return (m & 0x13) | ((m >> 1) & 0x4) | ((m << 1) & 0x8);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
+// lds + 16 * i (lds must be the same for the whole wave).  Reads past the
+// buffer's byte size return zeros.  (A plain, non-template device function: the
+// builtin inside a kernel template keeps the host pass from emitting the
+// kernel's launch stub.)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
 __device__ __forceinline__ float wave_halves_max(float x) {
@@ -78,13 +94,12 @@ __device__ __forceinline__ float wave_halves_sum(float x) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c,
     uint32_t qflip) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int TILE_CHUNKS = BC * CPR;      // chunks per K (or V) tile
-  constexpr int LD = TILE_CHUNKS / NT;       // chunks each thread moves per tile and tensor
   __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
 
   const int L = xcd_logical_id(blockIdx.x, total);
@@ -113,26 +128,27 @@ __global__ __launch_bounds__(NT) void attn_fwd_bf16_kernel(
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  uint4 kreg[LD], vreg[LD];
-  auto load_tile = [&](int j0) {
+  // Each wave issues LPW loads per tensor and tile: instruction i of wave w fills the 64
+  // consecutive 16-byte LDS slots starting at (i * NW + w) * 64; the lane picks
+  // the global chunk that the swizzled layout stores in its slot.
+  constexpr int NW = NT / 64;
+  constexpr int LPW = TILE_CHUNKS / NT;      // load instructions per wave per tensor
+  const uint32_t nbytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + hoff), 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + hoff), 0, nbytes, 0x00020000);
+  uint32_t lane_off[LPW];                    // byte offset of this lane's chunk within a tile
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int id = i * NT + tid, row = id / CPR, ch = id % CPR, key = j0 + row;
-      if (key < N) {
-        kreg[i] = *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + 8 * ch);
-        vreg[i] = *reinterpret_cast<const uint4*>(V + hoff + (size_t)key * D + 8 * ch);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int i = 0; i < LPW; ++i) {
+    const int pos = (i * NW + wave) * 64 + lane, row = pos / CPR, slot = pos % CPR;
+    lane_off[i] = (uint32_t)(row * D + 8 * (slot ^ swz<D>(row))) * 2;
+  }
+  auto issue_tile = [&](int j0, int buf) {
+    const uint32_t base = (uint32_t)j0 * D * 2;
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int id = i * NT + tid, row = id / CPR, ch = id % CPR;
-      smem[buf][0][lds_chunk<D>(row, ch)] = kreg[i];
-      smem[buf][1][lds_chunk<D>(row, ch)] = vreg[i];
+    for (int i = 0; i < LPW; ++i) {
+      const int slot0 = (i * NW + wave) * 64;
+      lds_dma16(krs, &smem[buf][0][slot0], base + lane_off[i]);
+      lds_dma16(vrs, &smem[buf][1][slot0], base + lane_off[i]);
     }
   };
 
@@ -144,14 +160,13 @@ __global__ __launch_bounds__(NT) void attn_fwd_bf16_kernel(
   float m2 = -INFINITY;   // reference maximum, exp2 domain (c * raw score)
   float lsum = 0.0f;      // this half-wave's share of the row sum
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  issue_tile(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BC;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(j0 + BC);
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's part of tile t has landed
+    __syncthreads();                         // ... and every other wave's; tile t-1's buffer is free
+    if (t + 1 < ntiles) issue_tile(j0 + BC, (t + 1) & 1);
 
     const bool active = !CAUSAL || j0 <= qw + 31;
     if (active) {
@@ -242,8 +257,6 @@ __global__ __launch_bounds__(NT) void attn_fwd_bf16_kernel(
       }
     }
 
-    if (has_next) store_tile((t + 1) & 1);
-    __syncthreads();
   }
 
   // epilogue: O = O / l, LSE = ln 2 * (m2 + log2 l)

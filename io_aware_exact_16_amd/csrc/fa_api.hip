@@ -31,6 +31,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;   // FP8 goes through fa_fwd_fp8
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, H, N, d, 64)) return FA_ERR_SHAPE;
+  if ((long long)N * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;   // one head's K or V must stay below 4 GiB
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
   if (o == q || o == k || o == v || (const void*)lse == q || (const void*)lse == k || (const void*)lse == v ||
       (void*)lse == o)
