@@ -46,6 +46,8 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 constexpr int BR = 128;   // query rows per workgroup
 constexpr int BC = 64;    // key rows per tile
@@ -75,12 +77,12 @@ __device__ __forceinline__ int key_of_arow(int m) {
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
-// lds + 16 * i (lds must be the same for the whole wave).  Reads past the
-// buffer's byte size return zeros.  (A plain, non-template device function: the
-// builtin inside a kernel template keeps the host pass from emitting the
-// kernel's launch stub.)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+// lds + 16 * i (lds must be the same for the whole wave).  The byte offset is
+// voffset (per lane) + soffset (per wave); reads past the buffer's byte size
+// return zeros.  (A plain device function: the builtin written inside a kernel
+// template keeps the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
 }
 
 __device__ __forceinline__ float wave_halves_max(float x) {
@@ -93,6 +95,104 @@ __device__ __forceinline__ float wave_halves_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+__device__ __forceinline__ bf16x4_t tr_read(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4_t, v);
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// One 64-key tile of one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+// kt / vt are the LDS K and V tiles; koff / voff are this lane's byte offsets
+// into them (first 32-key block, first 16-key chunk); MASK marks tiles that
+// cross the causal diagonal or the end of the sequence.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void tile_math(const char* kt, const char* vt, const uint32_t (&koff)[D / 16],
+                                          const uint32_t (&voff)[D / 32][2], const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&acc)[D / 32], float& m2, float& lsum, float c, int j0, int qi,
+                                          int N, int half) {
+  constexpr int KB_BYTES = 32 * D * 2;   // one 32-key block of the tile
+  constexpr int KC_BYTES = 16 * D * 2;   // one 16-key chunk of the tile
+  f32x16 s[BC / 32];
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[dc] + kb * KB_BYTES);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
+    }
+
+  __builtin_amdgcn_sched_barrier(0);
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
+        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+      }
+  }
+
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+  tmax = wave_halves_max(tmax);
+  const float tm2 = tmax * c;
+  if (__any(tm2 > m2 + RESCALE_THRESHOLD)) {
+    const float mnew = fmaxf(m2, tm2);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    lsum *= alpha;
+    m2 = mnew;
+  }
+
+  // p = exp2(c s - m2), rounded to bf16 as the B operand of P V; the row sum
+  // uses the float32 p (summing the bf16-rounded values would cost up to 2^-9
+  // relative in l, i.e. in LSE, on rows with few keys)
+  bf16x8 pb[BC / 16];
+  float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float s0 = s[kc >> 1][8 * (kc & 1) + e], s1 = s[kc >> 1][8 * (kc & 1) + e + 1];
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m2));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m2));
+      if (MASK) {                        // exact zeros for masked keys, also when c = 0
+        p0 = s0 == -INFINITY ? 0.0f : p0;
+        p1 = s1 == -INFINITY ? 0.0f : p1;
+      }
+      const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+      rs[e >> 1] += p0 + p1;
+      pb[kc][e] = pp[0];
+      pb[kc][e + 1] = pp[1];
+    }
+  lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16x4_t v0 = tr_read(vt + voff[db][0] + kc * KC_BYTES);
+      const bf16x4_t v1 = tr_read(vt + voff[db][1] + kc * KC_BYTES);
+      const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], acc[db], 0, 0, 0);
+    }
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -100,6 +200,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     uint32_t qflip) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int TILE_CHUNKS = BC * CPR;      // chunks per K (or V) tile
+  constexpr int NW = NT / 64;
+  constexpr int LPW = TILE_CHUNKS / NT;      // DMA instructions per wave, tensor and tile
   __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
 
   const int L = xcd_logical_id(blockIdx.x, total);
@@ -110,45 +212,59 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int qw = q0 + 32 * wave;             // first query row of this wave
+  const int qi = qw + l32;                   // this lane's query
   const size_t hoff = (size_t)bh * N * D;
 
-  // Q^T as the B operand: lane holds query qw + l32, dims 16*dc + 8*half + 0..7
+  // Q^T as the B operand: lane holds query qi, dims 16*dc + 8*half + 0..7
   bf16x8 qf[D / 16];
-  {
-    const int qi = qw + l32;
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qi < N) u = *reinterpret_cast<const uint4*>(Q + hoff + (size_t)qi * D + 16 * dc + 8 * half);
-      u.x ^= qflip; u.y ^= qflip; u.z ^= qflip; u.w ^= qflip;
-      qf[dc] = __builtin_bit_cast(bf16x8, u);
+  for (int dc = 0; dc < D / 16; ++dc) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (qi < N) u = *reinterpret_cast<const uint4*>(Q + hoff + (size_t)qi * D + 16 * dc + 8 * half);
+    u.x ^= qflip; u.y ^= qflip; u.z ^= qflip; u.w ^= qflip;
+    qf[dc] = __builtin_bit_cast(bf16x8, u);
+  }
+
+  // this lane's LDS byte offsets: K operand rows (first 32-key block) ...
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) koff[dc] = 16 * lds_chunk<D>(key_of_arow(l32), 2 * dc + half);
+  // ... and transposed V reads (first 16-key chunk; keys +0..3 and +4..7)
+  uint32_t voff[D / 32][2];
+  {
+    const int b16 = lane >> 4, j16 = lane & 15;
+    const int key = 8 * (b16 >> 1) + (j16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int dcol = 32 * db + 16 * (b16 & 1) + 4 * (j16 & 3);
+      voff[db][0] = 16 * lds_chunk<D>(key, dcol >> 3) + 2 * (dcol & 7);
+      voff[db][1] = 16 * lds_chunk<D>(key + 4, dcol >> 3) + 2 * (dcol & 7);
     }
   }
 
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
 
-  // Each wave issues LPW loads per tensor and tile: instruction i of wave w fills the 64
-  // consecutive 16-byte LDS slots starting at (i * NW + w) * 64; the lane picks
-  // the global chunk that the swizzled layout stores in its slot.
-  constexpr int NW = NT / 64;
-  constexpr int LPW = TILE_CHUNKS / NT;      // load instructions per wave per tensor
+  // DMA: instruction i of wave w fills the 64 consecutive 16-byte LDS slots
+  // starting at (i * NW + w) * 64; each lane loads the global chunk that the
+  // swizzled layout keeps in its slot.  The tile's start goes in soffset.
   const uint32_t nbytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + hoff), 0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + hoff), 0, nbytes, 0x00020000);
-  uint32_t lane_off[LPW];                    // byte offset of this lane's chunk within a tile
+  uint32_t lane_off[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int pos = (i * NW + wave) * 64 + lane, row = pos / CPR, slot = pos % CPR;
     lane_off[i] = (uint32_t)(row * D + 8 * (slot ^ swz<D>(row))) * 2;
   }
-  auto issue_tile = [&](int j0, int buf) {
+  auto issue_tile = [&](int j0, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const uint32_t base = (uint32_t)j0 * D * 2;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int slot0 = (i * NW + wave) * 64;
-      lds_dma16(krs, &smem[buf][0][slot0], base + lane_off[i]);
-      lds_dma16(vrs, &smem[buf][1][slot0], base + lane_off[i]);
+      lds_dma16(krs, &smem[BUF][0][slot0], lane_off[i], base);
+      lds_dma16(vrs, &smem[BUF][1][slot0], lane_off[i], base);
     }
   };
 
@@ -160,108 +276,29 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   float m2 = -INFINITY;   // reference maximum, exp2 domain (c * raw score)
   float lsum = 0.0f;      // this half-wave's share of the row sum
 
-  issue_tile(0, 0);
-
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int j0 = t * BC;
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's part of tile t has landed
-    __syncthreads();                         // ... and every other wave's; tile t-1's buffer is free
-    if (t + 1 < ntiles) issue_tile(j0 + BC, (t + 1) & 1);
+    __syncthreads();                         // ... and every other wave's; the other buffer is free
+    if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
+    if (CAUSAL && j0 > qw + 31) return;      // the whole tile is above this wave's diagonal
+    const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
+    const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
+    if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
+      tile_math<D, CAUSAL, true>(kt, vt, koff, voff, qf, acc, m2, lsum, c, j0, qi, N, half);
+    else
+      tile_math<D, CAUSAL, false>(kt, vt, koff, voff, qf, acc, m2, lsum, c, j0, qi, N, half);
+  };
 
-    const bool active = !CAUSAL || j0 <= qw + 31;
-    if (active) {
-      const uint4* Ks = smem[t & 1][0];
-      const uint4* Vs = smem[t & 1][1];
-
-      // S^T = K Q^T for the 64 keys of the tile, two 32-key blocks
-      f32x16 s[BC / 32];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-        const int row = 32 * kb + key_of_arow(l32);
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, Ks[lds_chunk<D>(row, 2 * dc + half)]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
-        }
-      }
-
-      // mask: keys past the end, and keys after the query on the diagonal
-      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
-      if (need_mask) {
-        const int qi = qw + l32;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
-            if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
-          }
-      }
-
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-      tmax = wave_halves_max(tmax);
-      const float tm2 = tmax * c;
-      if (__any(tm2 > m2 + RESCALE_THRESHOLD)) {
-        const float mnew = fmaxf(m2, tm2);
-        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        lsum *= alpha;
-        m2 = mnew;
-      }
-
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sv = s[kb][r];
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -m2));
-          if (need_mask && sv == -INFINITY) p = 0.0f;
-          s[kb][r] = p;
-          rs += p;
-        }
-      lsum += rs;
-
-      // O^T += V^T P^T, 16 keys per MFMA
-      const int b16 = lane >> 4, j16 = lane & 15;
-      const char* vbytes = reinterpret_cast<const char*>(Vs);
-#pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kc >> 1][8 * (kc & 1) + e];
-        const int key = 16 * kc + 8 * (b16 >> 1) + (j16 >> 2);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int dcol = 32 * db + 16 * (b16 & 1) + 4 * (j16 & 3);
-          const char* p0 = vbytes + 16 * lds_chunk<D>(key, dcol >> 3) + 2 * (dcol & 7);
-          const char* p1 = vbytes + 16 * lds_chunk<D>(key + 4, dcol >> 3) + 2 * (dcol & 7);
-          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(p0));
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(p1));
-          const short __attribute__((__vector_size__(8 * sizeof(short)))) vv = {
-              v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb, acc[db],
-                                                             0, 0, 0);
-        }
-      }
-    }
-
+  issue_tile(0, IC<0>{});
+  for (int t = 0; t < ntiles; t += 2) {     // unrolled by the two LDS buffers
+    step(t, IC<0>{});
+    if (t + 1 < ntiles) step(t + 1, IC<1>{});
   }
 
   // epilogue: O = O / l, LSE = ln 2 * (m2 + log2 l)
   const float ltot = wave_halves_sum(lsum);
-  const int qi = qw + l32;
   if (qi < N) {
     const float inv = 1.0f / ltot;
     uint16_t* orow = O + hoff + (size_t)qi * D;
@@ -270,10 +307,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = 32 * db + 8 * a + 4 * half;
-        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-        bf16x4 w = {(__bf16)(acc[db][4 * a + 0] * inv), (__bf16)(acc[db][4 * a + 1] * inv),
-                    (__bf16)(acc[db][4 * a + 2] * inv), (__bf16)(acc[db][4 * a + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(orow + d0) = w;
+        const bf16x4_t w = {(__bf16)(acc[db][4 * a + 0] * inv), (__bf16)(acc[db][4 * a + 1] * inv),
+                            (__bf16)(acc[db][4 * a + 2] * inv), (__bf16)(acc[db][4 * a + 3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(orow + d0) = w;
       }
     if (half == 0) LSE[(size_t)bh * N + qi] = (m2 + __log2f(ltot)) * 0.69314718055994531f;
   }
