@@ -36,8 +36,13 @@ Readings where the pages are silent:
     (for example y_u = 0.9375 in a block with amax 20 gives exactly 21), so
     both sides must round the same float32 quotient;
   - V is quantised per block the same way, without the Hadamard matrix;
-  - inside attention P is quantised as E4M3(256 p) / 256 with p = exp(S - m)
-    relative to the row maximum; the row sum l uses the unquantised p.
+  - inside attention P is quantised too (both products run on FP8 matrix
+    cores), with the per-block V scales folded into it: with
+    r_j = s_v(block of key j) / max over blocks of s_v (so 0 < r_j <= 1),
+    P_j is stored as E4M3(256 p_j r_j) and stands for E4M3(256 p_j r_j) /
+    (256 r_j); p = exp(S - m) relative to the row maximum, so 256 p r <= 256
+    stays inside E4M3 range and the power-of-two 256 keeps small p away from
+    the subnormals; the row sum l uses the unquantised p.
 """
 from __future__ import annotations
 
@@ -127,7 +132,8 @@ def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
 def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p: bool = True,
                   block: int = BLOCK):
     """Attention on dequantised FP8 operands, with P itself quantised as
-    E4M3(256 p)/256 when ``quantize_p`` (l from the unquantised p).
+    E4M3(256 p r)/(256 r) when ``quantize_p`` (r: the key's V-block scale over
+    the largest V-block scale of the head; l from the unquantised p).
     Returns (O, LSE) in float64."""
     q = dequantize_blocks(q8, qs, block)
     k = dequantize_blocks(k8, ks, block)
@@ -136,6 +142,7 @@ def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p
     idx = np.arange(N)
     o = np.empty((B, H, N, v.shape[3]))
     lse = np.empty((B, H, N))
+    vs64 = np.asarray(vs, dtype=np.float64)
     for b in range(B):
         for h in range(H):
             s = scale * (q[b, h] @ k[b, h].T)
@@ -144,7 +151,11 @@ def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p
             m = s.max(axis=1, keepdims=True)
             p = np.exp(s - m)
             l = p.sum(axis=1, keepdims=True)
-            pq = e4m3_decode(e4m3_encode(256.0 * p)) / 256.0 if quantize_p else p
+            if quantize_p:
+                r = np.repeat(vs64[b, h] / vs64[b, h].max(), block)[:N][None, :]
+                pq = e4m3_decode(e4m3_encode(256.0 * p * r)) / (256.0 * r)
+            else:
+                pq = p
             o[b, h] = (pq @ v[b, h]) / l
             lse[b, h] = (m + np.log(l))[:, 0]
     return o, lse

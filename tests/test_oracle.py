@@ -369,7 +369,8 @@ def test_attention_fp8_without_p_quant_is_plain_attention():
 
 
 def test_attention_fp8_p_quant_error_bound():
-    # each quantised p is within 2^-4 relative (normals) or 2^-18 absolute (subnormals of 256 p)
+    # each quantised p is within 2^-4 relative (normals) or 2^-10/(256 r) absolute
+    # (subnormals of 256 p r); here every V block has the same scale, so r = 1
     shape = (1, 1, 256, 128)
     q, k, v = (rng.standard_normal(shape) for _ in range(3))
     q8, qs = oracle.quantize_blocks(q, False)
@@ -378,8 +379,33 @@ def test_attention_fp8_p_quant_error_bound():
     o_q, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, False, quantize_p=True)
     o_n, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, False, quantize_p=False)
     vmax = np.abs(oracle.dequantize_blocks(v8, vs)).max()
-    assert np.abs(o_q - o_n).max() <= (2.0 ** -4 + 256 * 2.0 ** -18) * vmax
+    vs_eq = np.full_like(vs, vs.max())
+    o_q, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs_eq, 128 ** -0.5, False, quantize_p=True)
+    o_n, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs_eq, 128 ** -0.5, False, quantize_p=False)
+    assert np.abs(o_q - o_n).max() <= (2.0 ** -4 + 256 * 2.0 ** -18) * vmax * (vs_eq.max() / vs.min())
     assert np.abs(o_q - o_n).max() > 0
+
+
+def test_attention_fp8_p_quant_folds_v_block_scales():
+    # with unequal V-block scales, P is quantised as E4M3(256 p r)/(256 r): check
+    # one row against a scalar loop over its keys
+    shape = (1, 1, 256, 128)
+    q, k, v = (rng.standard_normal(shape) for _ in range(3))
+    v[:, :, 128:] *= 3.0                                   # second V block has a larger scale
+    q8, qs = oracle.quantize_blocks(q, False)
+    k8, ks = oracle.quantize_blocks(k, False)
+    v8, vs = oracle.quantize_blocks(v, False)
+    o, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 0.1, False, quantize_p=True)
+    qd, kd, vd = (oracle.dequantize_blocks(x, y) for x, y in ((q8, qs), (k8, ks), (v8, vs)))
+    i = 77
+    srow = 0.1 * (kd[0, 0] @ qd[0, 0, i])
+    p = np.exp(srow - srow.max())
+    num = np.zeros(128)
+    for j in range(256):
+        r = float(vs[0, 0, j // 128]) / float(vs[0, 0].max())
+        pq = float(oracle.e4m3_decode(oracle.e4m3_encode(256.0 * p[j] * r))) / (256.0 * r)
+        num += pq * vd[0, 0, j]
+    np.testing.assert_allclose(o[0, 0, i], num / p.sum(), rtol=0, atol=1e-12)
 
 
 def test_fp8_incoherent_processing_helps_at_1k_tokens():
