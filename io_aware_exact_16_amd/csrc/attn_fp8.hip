@@ -1,9 +1,326 @@
-// FP8 attention kernel: placeholder until the kernel lands; the entry point
-// reports a launch failure instead of computing anything.
+// Fused exact attention forward on per-block-scaled E4M3 operands, gfx950.
+//
+// The FP8 variant of the method ("FlashAttention-3 (PT)", section "Inovacoes
+// tecnicas", item 3: FP8 doubles the matrix throughput; Q and K are made
+// incoherent with an orthogonal Hadamard transform before quantisation, which
+// leaves Q K^T unchanged) with the same tiling / online softmax as the bf16
+// kernel ("Flash Attention" glossary page, second paragraph).
+//
+// Inputs are E4M3 codes with one float32 scale per (b, h, 128-token block).
+//  * S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales)
+//    over the codes; the two block scales fold into the softmax constant of
+//    the tile: c_t = |scale| log2(e) s_q s_k.
+//  * P is quantised to E4M3 for the second product as 256 p r_t with
+//    r_t = s_v(tile) / max_blocks s_v: the V-block scale rides in P, so one
+//    accumulator serves all V blocks and 256 p r <= 256 stays in range; the
+//    factor 256 r_t is folded into the exp2 argument (no extra multiply), and
+//    l accumulates p = P / (256 r_t) in float32.  O = acc * max s_v / (256 l).
+//  * The reference maximum moves whenever a tile's maximum exceeds it, so
+//    p <= 1 always.
+//  * Layouts as in the bf16 kernel (S^T and O^T accumulators; per-lane
+//    softmax state).  32x32x64 FP8 MFMA operands: lane l holds row (col)
+//    l % 32 and the 32 consecutive k values 32 * (l / 32) + 0..31.  V^T comes
+//    from the row-major LDS tile through ds_read_b64_tr_b8: within each
+//    16-lane group, lane 2r + c names the 8 bytes at [r][8c..8c+7] of an
+//    8 x 16 byte tile and lane j receives column j (verified on gfx950).
 #include "fa_internal.h"
+
 namespace fa {
-hipError_t launch_attn_fp8(const uint8_t*, const uint8_t*, const uint8_t*, const float*, const float*, const float*,
-                           void*, float*, int, int, int, float, bool, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int D = 128;    // head dimension (bytes per row)
+constexpr int BR = 128;   // query rows per workgroup = one scaling block
+constexpr int BC = 64;    // key rows per tile (half a scaling block)
+constexpr int NT = 256;   // threads per workgroup
+constexpr int QBLK = 128; // tokens per scaling block
+
+// Position (16-byte units) of chunk ch (0..7) of tile row `row` in LDS.  The
+// XOR swizzle makes both read patterns conflict-free: 16 lanes reading 16 B
+// of 16 different rows (K operand) and 32 lanes reading 8 B from 8 rows x 2
+// chunks (transposed V operand).
+__device__ __forceinline__ int lds_chunk8(int row, int ch) {
+  const int s = (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  return row * (D / 16) + (ch ^ s);
 }
+
+// Same A-row to key permutation as the bf16 kernel: the accumulator registers
+// 0..7 (8..15) of half-wave h then hold keys 8h + r (16 + 8h + r - 8).
+__device__ __forceinline__ int key_of_arow(int m) {
+  return (m & 0x13) | ((m >> 1) & 0x4) | ((m << 1) & 0x8);
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+}
+
+__device__ __forceinline__ i32x2 tr8_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // E4M3 x E4M3 (format code 0 for both), unit block scales (E8M0 127 = 2^0)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float wave_halves_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float wave_halves_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+constexpr int VMCNT(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+// One 64-key tile of one wave.  c_t: softmax constant of the tile (block
+// scales folded in); lr: log2(256 r_t); inv_r: 1 / (256 r_t).
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void tile_math(const char* kt, const char* vt, const uint32_t (&koff)[2][2],
+                                          const uint32_t (&voff)[4], const i32x8 (&qf)[2], f32x16 (&acc)[4],
+                                          float& m2, float& lsum, float c_t, float lr, float inv_r, int j0, int qi,
+                                          int N, int half) {
+  constexpr int KB_BYTES = 32 * D;   // one 32-key block of the tile
+  constexpr int KG_BYTES = 16 * D;   // 16 keys
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+  for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(kt + koff[dc][0] + kb * KB_BYTES);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(kt + koff[dc][1] + kb * KB_BYTES);
+      const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      s[kb] = mfma_fp8(a, qf[dc], s[kb]);
+    }
+
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
+        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+      }
+  }
+  float pm[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pm[kb] = fmaxf(pm[kb], s[kb][r]);
+  const float tm2 = wave_halves_max(fmaxf(pm[0], pm[1])) * c_t;
+  if (__any(tm2 > m2)) {                     // keep p <= 1: move the maximum whenever it grows
+    const float mnew = fmaxf(m2, tm2);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    lsum *= alpha;
+    m2 = mnew;
+  }
+
+  // P'' = 256 r_t exp2(c_t s - m2), quantised to E4M3 (round to nearest even);
+  // the byte for key slot e of the B operand comes from register (e / 16, e % 16)
+  const float off = lr - m2;
+  i32x8 pq;
+  float rs[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float p[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const float sv = s[w >> 2][4 * (w & 3) + y];
+      p[y] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c_t, off));
+      if (MASK) p[y] = sv == -INFINITY ? 0.0f : p[y];
+    }
+    rs[w & 1] += (p[0] + p[1]) + (p[2] + p[3]);
+    uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    pq[w] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], b, true);
+  }
+  lsum += (rs[0] + rs[1]) * inv_r;
+
+  // O^T += V^T P^T: the A operand for d-block db gathers keys 16g + 8h + 0..7 (g = 0..3)
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    i32x8 va;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const i32x2 v = tr8_read(vt + voff[db] + g * KG_BYTES);
+      va[2 * g] = v[0];
+      va[2 * g + 1] = v[1];
+    }
+    acc[db] = mfma_fp8(va, pq, acc[db]);
+  }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
+    const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c0, uint32_t qflip) {
+  constexpr int TILE_CHUNKS = BC * D / 16;   // 16-byte chunks per K (or V) tile
+  constexpr int NW = NT / 64;
+  constexpr int LPW = TILE_CHUNKS / NT;      // DMA instructions per wave, tensor and tile
+  __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
+
+  const int L = xcd_logical_id(blockIdx.x, total);
+  const int bh = L / nqb;
+  int qb = L - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;             // longest query blocks first
+  const int q0 = qb * BR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + l32;
+  const size_t hoff = (size_t)bh * N * D;
+  const int nsb = (N + QBLK - 1) / QBLK;     // scaling blocks per head
+  const float* vsh = VS + (size_t)bh * nsb;
+  const float* ksh = KS + (size_t)bh * nsb;
+
+  // largest V-block scale of the head (every lane of the wave ends with it)
+  float svmax = 0.0f;
+  for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, vsh[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) svmax = fmaxf(svmax, __shfl_xor(svmax, off));
+  const float c_q = c0 * QS[(size_t)bh * nsb + q0 / QBLK];
+
+  // Q^T as the B operand: lane holds query qi, bytes 64*dc + 32*half + 0..31
+  i32x8 qf[2];
+#pragma unroll
+  for (int dc = 0; dc < 2; ++dc) {
+    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+    if (qi < N) {
+      const uint4* src = reinterpret_cast<const uint4*>(Q8 + hoff + (size_t)qi * D + 64 * dc + 32 * half);
+      u0 = src[0];
+      u1 = src[1];
+    }
+    qf[dc] = i32x8{(int)(u0.x ^ qflip), (int)(u0.y ^ qflip), (int)(u0.z ^ qflip), (int)(u0.w ^ qflip),
+                   (int)(u1.x ^ qflip), (int)(u1.y ^ qflip), (int)(u1.z ^ qflip), (int)(u1.w ^ qflip)};
+  }
+
+  // this lane's LDS byte offsets: K operand rows (two 16-byte chunks per d-half) ...
+  uint32_t koff[2][2];
+#pragma unroll
+  for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) koff[dc][i] = 16 * lds_chunk8(key_of_arow(l32), 4 * dc + 2 * half + i);
+  // ... and 8-bit transposed V reads (keys 8*(G/2) + r of the first group, d-block db)
+  uint32_t voff[4];
+  {
+    const int G = lane >> 4, j = lane & 15, r = j >> 1, cc = j & 1;
+    const int key = 8 * (G >> 1) + r;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) voff[db] = 16 * lds_chunk8(key, 2 * db + (G & 1)) + 8 * cc;
+  }
+
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+
+  const uint32_t nbytes = (uint32_t)N * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K8 + hoff), 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V8 + hoff), 0, nbytes, 0x00020000);
+  uint32_t lane_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int pos = (i * NW + wave) * 64 + lane, row = pos / (D / 16), slot = pos % (D / 16);
+    const int sw = (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    lane_off[i] = (uint32_t)(row * D + 16 * (slot ^ sw));
+  }
+  auto issue_tile = [&](int j0, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const uint32_t base = (uint32_t)j0 * D;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int slot0 = (i * NW + wave) * 64;
+      lds_dma16(krs, &smem[BUF][0][slot0], lane_off[i], base);
+      lds_dma16(vrs, &smem[BUF][1][slot0], lane_off[i], base);
+    }
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m2 = -INFINITY, lsum = 0.0f;
+
+  auto step = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int j0 = t * BC;
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
+    if (CAUSAL && j0 > qw + 31) return;
+    const float ks = ksh[j0 / QBLK], r_t = vsh[j0 / QBLK] / svmax;
+    const float c_t = c_q * ks;
+    const float lr = 8.0f + __log2f(r_t);
+    const float inv_r = 1.0f / (256.0f * r_t);
+    const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
+    const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
+    if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
+      tile_math<CAUSAL, true>(kt, vt, koff, voff, qf, acc, m2, lsum, c_t, lr, inv_r, j0, qi, N, half);
+    else
+      tile_math<CAUSAL, false>(kt, vt, koff, voff, qf, acc, m2, lsum, c_t, lr, inv_r, j0, qi, N, half);
+  };
+
+  issue_tile(0, IC<0>{});
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, IC<0>{});
+    if (t + 1 < ntiles) step(t + 1, IC<1>{});
+  }
+
+  // epilogue: O = acc * max s_v / (256 l), LSE = ln 2 * (m2 + log2 l)
+  const float ltot = wave_halves_sum(lsum);
+  if (qi < N) {
+    const float f = svmax / (256.0f * ltot);
+    uint16_t* orow = O + hoff + (size_t)qi * D;
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * half;
+        const bf16x4_t w = {(__bf16)(acc[db][4 * a + 0] * f), (__bf16)(acc[db][4 * a + 1] * f),
+                            (__bf16)(acc[db][4 * a + 2] * f), (__bf16)(acc[db][4 * a + 3] * f)};
+        *reinterpret_cast<bf16x4_t*>(orow + d0) = w;
+      }
+    if (half == 0) LSE[(size_t)bh * N + qi] = (m2 + __log2f(ltot)) * 0.69314718055994531f;
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* qs, const float* ks,
+                  const float* vs, void* o, float* lse, int B, int H, int N, float scale, hipStream_t stream) {
+  const int nqb = (N + BR - 1) / BR;
+  const int total = nqb * H * B;
+  const float c0 = (float)((double)__builtin_fabsf(scale) * 1.4426950408889634);
+  const uint32_t qflip = scale < 0.0f ? 0x80808080u : 0u;
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(NT), 0, stream, q8, k8, v8, qs, ks, vs,
+                     static_cast<uint16_t*>(o), lse, N, nqb, total, c0, qflip);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* qs, const float* ks,
+                           const float* vs, void* o, float* lse, int B, int H, int N, float scale, bool causal,
+                           hipStream_t stream) {
+  return causal ? launch<true>(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, scale, stream)
+                : launch<false>(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, scale, stream);
+}
+
 }  // namespace fa

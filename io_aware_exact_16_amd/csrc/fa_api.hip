@@ -49,6 +49,7 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const fl
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, H, N, d, 64)) return FA_ERR_SHAPE;
+  if ((long long)N * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;   // same per-head limit as fa_fwd
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
   const void* ins[6] = {q8, k8, v8, q_scale, k_scale, v_scale};
   for (const void* p : ins)
