@@ -1,4 +1,7 @@
-// Fused exact attention forward, bf16 in / bf16 out, float32 softmax, gfx950.
+// Fused exact attention forward, bf16 in / bf16 out, float32 softmax, gfx950:
+// the streaming kernel (non-causal attention and head dimension 64; causal
+// attention with head dimension 128 runs the persistent ping-pong kernel of
+// attn_bf16_pp.hip, selected in launch_attn_bf16 below).
 //
 // Method ("Flash Attention" glossary page, second paragraph; "FlashAttention-3
 // (PT)", section "FlashAttention e FlashAttention-2"): one kernel walks the
@@ -32,78 +35,16 @@
 //    float32 and bf16 range, the final O / l and LSE are unchanged, and the
 //    O rescale (D/2 multiplies per lane) is skipped on almost every tile.
 //
-// Register-level layouts (lane l of 64, h = l / 32; verified on gfx950):
-//   32x32x16 bf16 MFMA: A[i][k] in lane (i + 32 * (k / 8)), element k % 8;
-//   B[k][j] in lane (j + 32 * (k / 8)), element k % 8; C[i][j] in lane
-//   (j + 32 * ((i / 4) % 2)), register 4 * (i / 8) + i % 4.
-//   ds_read_b64_tr_b16: within each 16-lane group, lane 4r + c names the 4
-//   elements at [r][4c..4c+3] of a 4 x 16 tile; lane j receives column j.
-#include "fa_internal.h"
+// The register layouts these rely on are listed in attn_bf16_common.h.
+#include "attn_bf16_common.h"
 
 namespace fa {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+using namespace bf16k;
 
 constexpr int BR = 128;   // query rows per workgroup
-constexpr int BC = 64;    // key rows per tile
 constexpr int NT = 256;   // threads per workgroup
-constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the allowed growth of p
-
-// Position (in 16-byte chunks) of chunk `ch` of tile row `row` in LDS.  The
-// XOR swizzle makes both read patterns of the kernel conflict-free: 16 lanes
-// reading 16 B from 16 different rows (K operand), and 32 lanes reading
-// 8 B from 4 rows x 4 chunks (transposed V operand).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  return (D == 128) ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-}
-
-template <int D>
-__device__ __forceinline__ int lds_chunk(int row, int ch) {
-  return row * (D / 8) + (ch ^ swz<D>(row));
-}
-
-// Row of a 32-key block that A-operand row m must hold so that, in the
-// accumulator layout, the 8 registers r = 0..7 (8..15) of half-wave h hold keys
-// 8h + r (16 + 8h + r - 8): consecutive keys, ready to be the B operand of P V.
-// It swaps bits 2 and 3 of m.
-__device__ __forceinline__ int key_of_arow(int m) {
-  return (m & 0x13) | ((m >> 1) & 0x4) | ((m << 1) & 0x8);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
-// lds + 16 * i (lds must be the same for the whole wave).  The byte offset is
-// voffset (per lane) + soffset (per wave); reads past the buffer's byte size
-// return zeros.  (A plain device function: the builtin written inside a kernel
-// template keeps the host pass from emitting the kernel's launch stub.)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
-}
-
-__device__ __forceinline__ float wave_halves_max(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-
-__device__ __forceinline__ float wave_halves_sum(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-__device__ __forceinline__ bf16x4_t tr_read(const char* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(bf16x4_t, v);
-}
-
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
 
 // One 64-key tile of one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
 // kt / vt are the LDS K and V tiles; koff / voff are this lane's byte offsets
@@ -357,7 +298,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                             int N, int d, float scale, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
+  if (d == 128) return causal ? launch_attn_bf16_pp(q, k, v, o, lse, B, H, N, scale, stream)
                               : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
   return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
                 : launch<64, false>(q, k, v, o, lse, B, H, N, scale, stream);

@@ -10,6 +10,10 @@ namespace fa {
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
 
+// Causal attention, head dimension 128: the persistent ping-pong kernel.
+hipError_t launch_attn_bf16_pp(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, float scale, hipStream_t stream);
+
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
 

@@ -67,6 +67,25 @@ def test_workload_sampled_rows(gpu, name):
     log(f"  max|dO|={e[0]:.3g} max rel dLSE={e[1]:.3g}")
 
 
+@pytest.mark.parametrize("B,H,N,scale_mult", [
+    (2, 16, 8192, 1.0),    # 32 heads x 32 blocks of 256 rows: 4 items per persistent workgroup, heads grouped per XCD
+    (3, 5, 5000, 1.0),     # 15 heads (not a multiple of 8): global item order; 5000 % 256 = 136: odd tile count
+    (1, 8, 1024, -1.0),    # fewer items than compute units; negative scale
+])
+def test_causal_d128_every_work_item(gpu, B, H, N, scale_mult):
+    """Causal d = 128 runs the persistent kernel: rows from every 256-row block of every head."""
+    w = custom(B, H, N, 128, True, "bf16", seed=N + 31 * H + B)
+    scale = w.scale * scale_mult
+    q, k, v = make_qkv(w)
+    log(f"[persistent] B={B} H={H} N={N} scale={scale:.4f}")
+    o, lse = run_attention(q, k, v, True, scale)
+    rows = np.unique(np.array([r for b0 in range(0, N, 256) for r in (b0, b0 + 37, b0 + 128, b0 + 255)] + [N - 1]))
+    rows = rows[rows < N]
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    e = compare_sampled(q, k, v, o, lse, True, scale, "bf16", heads, rows)
+    log(f"  {len(heads)} heads x {len(rows)} rows: max|dO|={e[0]:.3g} max rel dLSE={e[1]:.3g}")
+
+
 def test_long_context_allocates_nothing(gpu):
     w = WORKLOADS["bf16_causal_32k"]
     q, k, v = to_dev(*make_qkv(w))
