@@ -34,7 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense, published
-KERNEL_SOURCE = {"bf16": "attn_bf16.hip", "fp8": "attn_fp8.hip", "f32": "attn_f32.hip"}
+
+
+def kernel_source(w) -> str:
+    """Source file of the attention kernel that runs this workload."""
+    if w.dtype == "bf16":
+        return "attn_bf16_pp.hip" if (w.causal and w.d == 128) else "attn_bf16.hip"
+    return {"fp8": "attn_fp8.hip", "f32": "attn_f32.hip"}[w.dtype]
 
 
 def eprint(*a):
@@ -178,7 +184,7 @@ def main() -> int:
     dtype = w.dtype
     peak = PEAK_TFLOPS[dtype]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, KERNEL_SOURCE[dtype])}
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, kernel_source(w))}
     eprint(f"[bench] {w.name}: step {ms_per_step:.4f} ms, attention kernel avg {kern_avg_ms:.4f} ms "
            f"(min {min(kern_ms):.4f}), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} peak")
 
