@@ -7,22 +7,29 @@
 // matrix of order d scaled by 1/sqrt(d), applied to every token row with a fast
 // Walsh-Hadamard transform (log2 d butterfly stages).
 //
-// One workgroup per (batch, head, block of 128 tokens) -- the scaling
+// Work unit: one (batch, head, block of 128 tokens) -- the scaling
 // granularity -- so the block maximum is a workgroup reduction and every byte
-// is read from and written to HBM exactly once.  The kernel is bound by HBM
-// bandwidth; arithmetic is chosen for reproducibility instead of speed:
+// is read from and written to HBM exactly once.  Arithmetic is chosen for
+// reproducibility:
 //  * the butterflies run in float64: sums of +-bf16 (or fp32) values are then
 //    exact, so the transformed values y_u = x H do not depend on the order of
-//    the butterflies (on gfx950 unpacked float64 adds issue at the float32 rate);
+//    the butterflies; without the transform y_u = x is exact in float32, which
+//    the plain kernel uses;
 //  * the rounding decision is taken on the float32 quotient
 //    RN32(y_u) * RN32(448 / RN32(A)), A = max |y_u| over the block (the 1/sqrt(d)
 //    of the matrix cancels in y / s), plus 0 so that a zero quotient is +0;
 //    v_cvt_pk_fp8_f32 rounds to nearest even;
 //  * the stored scale is s = A / (448 sqrt(d)) (A / 448 without the matrix),
 //    rounded once from float64 to float32; s = 1 for an all-zero block.
-// Coalesced 16-byte loads land in a padded LDS tile; each thread then owns 64
-// consecutive elements of one row (2 threads per row at d = 128), so 6 of the
-// 7 butterfly stages are in registers and the last is one DPP lane swap.
+//
+// Transform kernel, streaming (meant to run at HBM bandwidth): a persistent grid
+// walks the blocks; each workgroup DMAs the next block's tile HBM -> LDS
+// (buffer_load ... lds, XOR-swizzled rows, rows past N read as zeros) while it
+// transforms the current one, and holds its E4M3 bytes in registers until the
+// next block's wait, so no wait ever covers a store it has just issued.  In the
+// tile each thread owns 64 consecutive elements of one row (2 threads per row
+// at d = 128): 6 of the 7 butterfly stages are in registers, the last is one
+// DPP lane swap.
 #include "fa_internal.h"
 
 namespace fa {
@@ -31,92 +38,128 @@ namespace {
 constexpr int BLK = 128;   // tokens per scaling block
 constexpr int EPT = 64;    // elements per thread
 
-template <int D, bool BF16IN, bool HAD>
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+}
+
+template <int D, bool BF16IN>
 __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const void* __restrict__ X,
                                                                    uint8_t* __restrict__ X8,
                                                                    float* __restrict__ S, int N, int nb,
-                                                                   double denom) {
+                                                                   int nblocks, double denom) {
+  using T = double;
   constexpr int NT = 2 * D;                  // threads: 128 rows x (D / 64) threads per row
+  constexpr int NW = NT / 64;
   constexpr int TPR = D / EPT;
   constexpr int ES = BF16IN ? 2 : 4;         // input element size
-  constexpr int ROWB = D * ES + 16;          // padded LDS row stride in bytes
   constexpr int CPR = D * ES / 16;           // 16-byte chunks per input row
-  constexpr int LDC = BLK * CPR / NT;        // chunks loaded per thread
-  __shared__ __attribute__((aligned(16))) char tile[BLK * ROWB];
-  __shared__ double wmax[NT / 64];
+  constexpr int TILE = BLK * CPR;            // chunks per tile
+  constexpr int LPT = TILE / NT;             // DMA instructions per thread and tile
+  constexpr int CPT = EPT * ES / 16;         // chunks read per thread
+  // chunk c of tile row r sits at r * CPR + (c ^ (r & 7)): conflict-free reads
+  // of each thread's 64-element segment
+  __shared__ uint4 tile0[TILE], tile1[TILE];
+  __shared__ double wmax[NW];
 
-  const int bh = blockIdx.x / nb, jb = blockIdx.x % nb;
-  const int r0 = jb * BLK, tid = threadIdx.x;
-  const size_t hoff = (size_t)bh * N * D;
-  const char* xb = static_cast<const char*>(X) + hoff * ES;
-
-#pragma unroll
-  for (int i = 0; i < LDC; ++i) {
-    const int c = i * NT + tid, row = c / CPR, cc = c % CPR;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (r0 + row < N) u = *reinterpret_cast<const uint4*>(xb + ((size_t)(r0 + row) * D) * ES + 16 * cc);
-    *reinterpret_cast<uint4*>(tile + row * ROWB + 16 * cc) = u;
-  }
-  __syncthreads();
-
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = tid / TPR, part = tid % TPR;
-  double x[EPT];
-  {
-    const char* src = tile + row * ROWB + part * EPT * ES;
+
+  // DMA: instruction i of wave w fills slots (i * NW + w) * 64 + lane
+  uint32_t lane_off[LPT];
 #pragma unroll
-    for (int i = 0; i < EPT * ES / 16; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src + 16 * i);
+  for (int i = 0; i < LPT; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane, r = slot / CPR, c = (slot % CPR) ^ (r & 7);
+    lane_off[i] = (uint32_t)(r * D * ES + 16 * c);
+  }
+  auto issue = [&](int blk, uint4* dst) {
+    const int bh = blk / nb, jb = blk - bh * nb;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const char*>(X) + (size_t)bh * N * D * ES), 0, (uint32_t)N * D * ES, 0x00020000);
+    const uint32_t base = (uint32_t)(jb * BLK) * D * ES;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) lds_dma16(rs, dst + (i * NW + wave) * 64, lane_off[i], base);
+  };
+
+  // the previous block's results, stored once the next block's wait is done
+  uint4 held[EPT / 16];
+  uint8_t* held_dst = nullptr;
+  float held_scale = 0.0f;
+  float* held_sdst = nullptr;
+  auto flush = [&]() {
+    if (held_dst) {
+#pragma unroll
+      for (int i = 0; i < EPT / 16; ++i) *reinterpret_cast<uint4*>(held_dst + 16 * i) = held[i];
+    }
+    if (held_sdst) *held_sdst = held_scale;
+  };
+
+  // one block: its tile is in cur (its DMA is complete after the wait below),
+  // the next block's tile goes to nxt; cur and nxt are distinct arrays at every
+  // call, so the compiler never orders the reads of cur behind the DMA into nxt
+  auto block = [&](int blk, const uint4* cur, uint4* nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's part of the tile (and older stores)
+    __syncthreads();                         // ... every thread's part; everyone is done with nxt
+    if (blk + (int)gridDim.x < nblocks) issue(blk + gridDim.x, nxt);
+    flush();
+
+    const int bh = blk / nb, jb = blk - bh * nb;
+    const int r0 = jb * BLK;
+    T x[EPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const uint4 u = cur[row * CPR + ((part * CPT + i) ^ (row & 7))];
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (BF16IN) {
-          x[8 * i + 2 * j] = (double)__uint_as_float(w[j] << 16);
-          x[8 * i + 2 * j + 1] = (double)__uint_as_float(w[j] & 0xffff0000u);
+          x[8 * i + 2 * j] = (T)__uint_as_float(w[j] << 16);
+          x[8 * i + 2 * j + 1] = (T)__uint_as_float(w[j] & 0xffff0000u);
         } else {
-          x[4 * i + j] = (double)__uint_as_float(w[j]);
+          x[4 * i + j] = (T)__uint_as_float(w[j]);
         }
       }
     }
-  }
 
-  if (HAD) {
+    {
 #pragma unroll
-    for (int s = 1; s < EPT; s <<= 1)
+      for (int s = 1; s < EPT; s <<= 1)
 #pragma unroll
-      for (int i = 0; i < EPT; ++i)
-        if (!(i & s)) {
-          const double a = x[i], b = x[i + s];
-          x[i] = a + b;
-          x[i + s] = a - b;
+        for (int i = 0; i < EPT; ++i)
+          if (!(i & s)) {
+            const T a = x[i], b = x[i + s];
+            x[i] = a + b;
+            x[i + s] = a - b;
+          }
+      if (TPR == 2) {   // stride-64 stage: partner element sits in the adjacent lane
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const uint64_t bits = __double_as_longlong((double)x[i]);
+          const uint32_t lo = __builtin_amdgcn_update_dpp(0, (uint32_t)bits, 0xB1, 0xF, 0xF, false);
+          const uint32_t hi = __builtin_amdgcn_update_dpp(0, (uint32_t)(bits >> 32), 0xB1, 0xF, 0xF, false);
+          const T other = (T)__longlong_as_double(((uint64_t)hi << 32) | lo);
+          x[i] = part == 0 ? x[i] + other : other - x[i];
         }
-    if (TPR == 2) {   // stride-64 stage: partner element sits in the adjacent lane
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const uint64_t bits = __double_as_longlong(x[i]);
-        const uint32_t lo = __builtin_amdgcn_update_dpp(0, (uint32_t)bits, 0xB1, 0xF, 0xF, false);
-        const uint32_t hi = __builtin_amdgcn_update_dpp(0, (uint32_t)(bits >> 32), 0xB1, 0xF, 0xF, false);
-        const double other = __longlong_as_double(((uint64_t)hi << 32) | lo);
-        x[i] = part == 0 ? x[i] + other : other - x[i];
       }
     }
-  }
 
-  double amax = 0.0;
+    T amax = 0;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) amax = fmax(amax, fabs(x[i]));
-  if (r0 + row >= N) amax = 0.0;
+    for (int i = 0; i < EPT; ++i) amax = fmax(amax, fabs(x[i]));
+    if (r0 + row >= N) amax = 0;
+    double amax64 = (double)amax;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmax(amax, __shfl_xor(amax, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
-  __syncthreads();
-  double A = wmax[0];
+    for (int off = 32; off > 0; off >>= 1) amax64 = fmax(amax64, __shfl_xor(amax64, off));
+    if (lane == 0) wmax[wave] = amax64;
+    // the waves' maxima are in LDS; a bare barrier, so that the prefetch DMA
+    // and the stores issued above stay in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+    __asm__ volatile("s_barrier" ::: "memory");
+    double A = wmax[0];
 #pragma unroll
-  for (int w = 1; w < NT / 64; ++w) A = fmax(A, wmax[w]);
+    for (int w = 1; w < NW; ++w) A = fmax(A, wmax[w]);
 
-  const float a32 = (float)A;
-  const float inv32 = a32 > 0.0f ? 448.0f / a32 : 0.0f;
-  if (r0 + row < N) {
-    uint8_t* dst = X8 + hoff + (size_t)(r0 + row) * D + part * EPT;
+    const float a32 = (float)A;
+    const float inv32 = a32 > 0.0f ? 448.0f / a32 : 0.0f;
 #pragma unroll
     for (int i = 0; i < EPT / 16; ++i) {
       uint32_t w[4];
@@ -128,18 +171,125 @@ __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const void* _
         uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
         w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, p, true);
       }
-      *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(w[0], w[1], w[2], w[3]);
+      held[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    held_dst = r0 + row < N ? X8 + (size_t)bh * N * D + (size_t)(r0 + row) * D + part * EPT : nullptr;
+    held_sdst = tid == 0 ? S + (size_t)bh * nb + jb : nullptr;
+    held_scale = A > 0.0 ? (float)(A / denom) : 1.0f;
+  };
+
+  int blk = blockIdx.x;
+  if (blk < nblocks) issue(blk, tile0);
+  while (blk < nblocks) {                    // unrolled over the two tiles
+    block(blk, tile0, tile1);
+    blk += gridDim.x;
+    if (blk >= nblocks) break;
+    block(blk, tile1, tile0);
+    blk += gridDim.x;
   }
-  if (tid == 0) S[(size_t)bh * nb + jb] = A > 0.0 ? (float)(A / denom) : 1.0f;
+  flush();
 }
 
-template <int D, bool BF16IN, bool HAD>
+// Without the transform the scale is the maximum over the whole block, so no
+// thread needs a whole row: each thread quantises whole 16-byte input chunks
+// (fully coalesced loads straight into registers, no LDS tile), the maximum is
+// a workgroup reduction, and the codes go out as coalesced stores.  Values stay
+// in float32, where bf16 and fp32 inputs are exact.  Few registers, so many
+// blocks' loads are in flight per compute unit.
+template <int D, bool BF16IN>
+__global__ __launch_bounds__(256) void fp8_quant_plain_kernel(const void* __restrict__ X, uint8_t* __restrict__ X8,
+                                                              float* __restrict__ S, int N, int nb) {
+  constexpr int NT = 256, NW = NT / 64;
+  constexpr int ES = BF16IN ? 2 : 4;
+  constexpr int EPC = 16 / ES;                   // elements per 16-byte chunk
+  constexpr int CHUNKS = BLK * D / EPC;          // chunks per block
+  constexpr int CPT = CHUNKS / NT;               // chunks per thread
+  __shared__ float wmax[NW];
+  const int bh = blockIdx.x / nb, jb = blockIdx.x - bh * nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t e0 = ((size_t)bh * N + (size_t)jb * BLK) * D;   // first element of the block
+  const size_t nvalid = (size_t)min(BLK, N - jb * BLK) * D;     // elements of the block inside the tensor
+  const char* xb = static_cast<const char*>(X) + e0 * ES;
+
+  uint4 u[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * NT + tid;                  // consecutive threads, consecutive chunks
+    u[i] = (size_t)c * EPC < nvalid ? *reinterpret_cast<const uint4*>(xb + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (BF16IN) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xffff0000u)));
+      } else {
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[j])));
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  float A = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) A = fmaxf(A, wmax[w]);
+
+  const float inv32 = A > 0.0f ? 448.0f / A : 0.0f;
+  uint8_t* dst = X8 + e0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = i * NT + tid;
+    if ((size_t)c * EPC >= nvalid) continue;
+    const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+    if (BF16IN) {                                // 8 elements -> 8 codes
+      uint32_t o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float q0 = __uint_as_float(w[2 * h] << 16) * inv32 + 0.0f;
+        const float q1 = __uint_as_float(w[2 * h] & 0xffff0000u) * inv32 + 0.0f;
+        const float q2 = __uint_as_float(w[2 * h + 1] << 16) * inv32 + 0.0f;
+        const float q3 = __uint_as_float(w[2 * h + 1] & 0xffff0000u) * inv32 + 0.0f;
+        const uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+        o[h] = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, p, true);
+      }
+      *reinterpret_cast<uint2*>(dst + (size_t)c * EPC) = make_uint2(o[0], o[1]);
+    } else {                                     // 4 elements -> 4 codes
+      const float q0 = __uint_as_float(w[0]) * inv32 + 0.0f, q1 = __uint_as_float(w[1]) * inv32 + 0.0f;
+      const float q2 = __uint_as_float(w[2]) * inv32 + 0.0f, q3 = __uint_as_float(w[3]) * inv32 + 0.0f;
+      const uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+      *reinterpret_cast<uint32_t*>(dst + (size_t)c * EPC) = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, p, true);
+    }
+  }
+  if (tid == 0) S[(size_t)bh * nb + jb] = A > 0.0f ? (float)((double)A / 448.0) : 1.0f;
+}
+
+template <int D, bool BF16IN>
 hipError_t launch(const void* x, uint8_t* x8, float* s, int B, int H, int N, hipStream_t stream) {
   const int nb = (N + BLK - 1) / BLK;
-  const double denom = HAD ? 448.0 * __builtin_sqrt((double)D) : 448.0;
-  hipLaunchKernelGGL((hadamard_fp8_quant_kernel<D, BF16IN, HAD>), dim3(nb * H * B), dim3(2 * D), 0, stream, x,
-                     x8, s, N, nb, denom);
+  const int nblocks = nb * H * B;
+  const double denom = 448.0 * __builtin_sqrt((double)D);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, hadamard_fp8_quant_kernel<D, BF16IN>, 2 * D, 0);
+  if (e != hipSuccess) return e;
+  const long slots = (long)cus * (per_cu > 0 ? per_cu : 1);
+  const int grid = nblocks < slots ? nblocks : (int)slots;
+  hipLaunchKernelGGL((hadamard_fp8_quant_kernel<D, BF16IN>), dim3(grid), dim3(2 * D), 0, stream, x, x8, s, N,
+                     nb, nblocks, denom);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16IN>
+hipError_t launch_plain(const void* x, uint8_t* x8, float* s, int B, int H, int N, hipStream_t stream) {
+  const int nb = (N + BLK - 1) / BLK;
+  hipLaunchKernelGGL((fp8_quant_plain_kernel<D, BF16IN>), dim3(nb * H * B), dim3(256), 0, stream, x, x8, s, N, nb);
   return hipGetLastError();
 }
 
@@ -147,14 +297,14 @@ hipError_t launch(const void* x, uint8_t* x8, float* s, int B, int H, int N, hip
 
 hipError_t launch_hadamard_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8, float* scales, int B, int H,
                                      int N, int d, bool hadamard, hipStream_t stream) {
-  if (d == 128) {
-    if (x_is_bf16) return hadamard ? launch<128, true, true>(x, x8, scales, B, H, N, stream)
-                                   : launch<128, true, false>(x, x8, scales, B, H, N, stream);
-    return hadamard ? launch<128, false, true>(x, x8, scales, B, H, N, stream)
-                    : launch<128, false, false>(x, x8, scales, B, H, N, stream);
-  }
-  return x_is_bf16 ? launch<64, true, false>(x, x8, scales, B, H, N, stream)
-                   : launch<64, false, false>(x, x8, scales, B, H, N, stream);
+  if (hadamard)   // d = 128 (checked by the entry point)
+    return x_is_bf16 ? launch<128, true>(x, x8, scales, B, H, N, stream)
+                     : launch<128, false>(x, x8, scales, B, H, N, stream);
+  if (d == 128)
+    return x_is_bf16 ? launch_plain<128, true>(x, x8, scales, B, H, N, stream)
+                     : launch_plain<128, false>(x, x8, scales, B, H, N, stream);
+  return x_is_bf16 ? launch_plain<64, true>(x, x8, scales, B, H, N, stream)
+                   : launch_plain<64, false>(x, x8, scales, B, H, N, stream);
 }
 
 }  // namespace fa
