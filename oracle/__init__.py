@@ -7,6 +7,9 @@ nothing here imports them: the two implementations share no code.
 
   attention.attention  -- softmax(scale Q K^T + causal mask) V and LSE, by the
                           definition (full score rows, float64)
+  merge.lse_merge      -- combine partial attentions over disjoint key sets
+                          through their LSEs; merge.decode_positions gives the
+                          query positions of a decode step
   fp8.*                -- Sylvester Hadamard matrix, E4M3 encode/decode from
                           the bit layout, per-block quantisation, and attention
                           on dequantised FP8 operands
@@ -15,8 +18,9 @@ Every function is pinned by tests against closed forms, special cases,
 brute force and library routines; none is marked "parity unpinned".
 """
 from .attention import attention
+from .merge import lse_merge, decode_positions
 from .fp8 import (sylvester_hadamard, orthonormal_hadamard, e4m3_decode, e4m3_encode,
                   quantize_blocks, dequantize_blocks, attention_fp8, E4M3_MAX, BLOCK)
 
-__all__ = ["attention", "sylvester_hadamard", "orthonormal_hadamard", "e4m3_decode", "e4m3_encode",
+__all__ = ["attention", "lse_merge", "decode_positions", "sylvester_hadamard", "orthonormal_hadamard", "e4m3_decode", "e4m3_encode",
            "quantize_blocks", "dequantize_blocks", "attention_fp8", "E4M3_MAX", "BLOCK"]

@@ -170,6 +170,43 @@ def test_split_keys_merge_identity():
     np.testing.assert_allclose(m + np.log(w1 + w2), lse, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_merge_of_key_chunks_is_full_attention(causal):
+    # decode-shaped rows (the last Nq positions of Nk tokens) against key chunks of
+    # uneven sizes; causal chunks see the keys at their absolute positions
+    Nq, Nk, d = 5, 97, 16
+    q, k, v = rng.standard_normal((1, 2, Nq, d)), rng.standard_normal((1, 2, Nk, d)), rng.standard_normal((1, 2, Nk, d))
+    pos = oracle.decode_positions(Nq, Nk)
+    assert list(pos) == list(range(Nk - Nq, Nk))
+    o, lse = attention(q, k, v, 0.3, causal, q_index=pos)
+    cuts = [0, 13, 40, 41, 90, Nk]
+    parts = [attention(q, k[:, :, a:b], v[:, :, a:b], 0.3, causal, q_index=pos - a) for a, b in zip(cuts, cuts[1:])]
+    om, lm = oracle.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, lse, atol=1e-13)
+
+
+def test_lse_merge_special_cases():
+    o1 = rng.standard_normal((2, 3, 8))
+    l1 = rng.standard_normal((2, 3))
+    om, lm = oracle.lse_merge(o1[None], l1[None])                     # one part: identity
+    np.testing.assert_allclose(om, o1, atol=1e-15)
+    np.testing.assert_allclose(lm, l1, atol=1e-15)
+    om, lm = oracle.lse_merge(np.stack([o1, o1]), np.stack([l1, l1]))  # two equal parts: LSE + ln 2
+    np.testing.assert_allclose(om, o1, atol=1e-15)
+    np.testing.assert_allclose(lm, l1 + math.log(2.0), atol=1e-15)
+    junk = np.full_like(o1, 1e30)                                      # a part that saw no key
+    om, lm = oracle.lse_merge(np.stack([junk, o1]), np.stack([np.full_like(l1, -np.inf), l1]))
+    np.testing.assert_allclose(om, o1, atol=1e-15)
+    np.testing.assert_allclose(lm, l1, atol=1e-15)
+    om, lm = oracle.lse_merge(np.stack([junk]), np.stack([np.full_like(l1, -np.inf)]))  # nothing visible
+    assert np.all(om == 0) and np.all(lm == -np.inf)
+    # hand-derived: parts with LSE ln 1 and ln 3 weigh 1/4 and 3/4
+    om, lm = oracle.lse_merge(np.array([[[2.0]], [[6.0]]]), np.array([[0.0], [math.log(3.0)]]))
+    np.testing.assert_allclose(om, [[5.0]], atol=1e-15)
+    np.testing.assert_allclose(lm, [math.log(4.0)], atol=1e-15)
+
+
 def test_row_subset_matches_full():
     N, d = 300, 16
     q, k, v = (rng.standard_normal((1, 2, N, d)) for _ in range(3))
