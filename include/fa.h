@@ -32,7 +32,8 @@
  *             enqueued asynchronously on it; the call never synchronises.
  *             Results are valid once the caller has synchronised that stream.
  *   Memory:   the library allocates nothing and keeps no mutable global state;
- *             concurrent calls from several host threads are safe.
+ *             concurrent calls from several host threads are safe (fa_fwd_decode
+ *             takes its scratch space from the caller).
  *   Errors:   arguments are checked before any HIP call.  On a negative status
  *             nothing has been enqueued and the outputs are untouched, except
  *             FA_ERR_LAUNCH, which reports a failed kernel launch.  Device
@@ -43,6 +44,7 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -63,7 +65,8 @@ enum fa_status {
   FA_ERR_DTYPE = -3,        /* unknown dtype code, or FA_FP8_E4M3 passed to fa_fwd */
   FA_ERR_UNSUPPORTED = -4,  /* head dimension not supported for this dtype/entry point */
   FA_ERR_LAUNCH = -5,       /* the kernel launch failed (hipGetLastError) */
-  FA_ERR_ARG = -6           /* non-finite scale, flag not 0/1, or an output aliasing an input */
+  FA_ERR_ARG = -6           /* non-finite scale, flag not 0/1, an output aliasing an input, or a
+                               workspace smaller than required */
 };
 
 /*
@@ -115,6 +118,53 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  */
 int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scales,
                           int B, int H, int N, int d, int hadamard, void* stream);
+
+/*
+ * Split-KV forward for a few queries against a long key sequence (a decode
+ * step of long-context inference), and the merge of partial attentions.
+ * "Flash Attention" glossary page, second paragraph: the online softmax
+ * accumulates partial results block by block; fourth paragraph: ring attention
+ * spreads the tiling over devices.  Both rest on the identity, for disjoint
+ * key parts p with partial results O_p (normalised by their own sum) and LSE_p:
+ *     LSE = ln sum_p exp(LSE_p),    O = sum_p exp(LSE_p - LSE) O_p.
+ */
+
+/*
+ * fa_fwd_decode_workspace_bytes -- device workspace fa_fwd_decode needs for
+ * these sizes (0 when the sizes are invalid).  Host-only; no HIP call.
+ */
+size_t fa_fwd_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * fa_fwd_decode -- attention of Nq queries against Nk keys, bfloat16.
+ *   q          : [B,H,Nq,d] bf16;  k, v : [B,H,Nk,d] bf16;  d is 64 or 128.
+ *   o          : [B,H,Nq,d] bf16 output;  lse : [B,H,Nq] float32 output.
+ *   causal     : 0 or 1.  With 1 the queries are the last Nq of the Nk tokens:
+ *                query i sits at position Nk - Nq + i and sees keys
+ *                0 .. Nk - Nq + i (Nq <= Nk is required).
+ *   workspace  : caller-owned device buffer of at least
+ *                fa_fwd_decode_workspace_bytes(B,H,Nq,Nk,d) bytes; its contents
+ *                are overwritten and meaningless afterwards.  Calls that share a
+ *                workspace must not run concurrently.
+ * The keys are cut into chunks; one kernel writes every chunk's partial O
+ * (float32) and LSE into the workspace, a second merges them (two launches on
+ * `stream`).  The result equals fa_fwd on the same rows up to rounding.
+ */
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_lse_merge -- combine P partial attentions of the same queries over
+ * disjoint key sets (for instance the shards of ring attention).
+ *   o_parts    : [P,B,H,N,d] float32, part p normalised by its own sum.
+ *   lse_parts  : [P,B,H,N] float32, natural-log units; -inf marks a part in
+ *                which the row saw no key (that part is ignored).
+ *   o          : [B,H,N,d] output, o_dtype FA_F32 or FA_BF16;  lse : [B,H,N] float32.
+ *   d          : 64 or 128.  A row whose parts are all -inf gets O = 0, LSE = -inf.
+ */
+int fa_lse_merge(const float* o_parts, const float* lse_parts, int P, int B, int H, int N, int d,
+                 void* o, int o_dtype, float* lse, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

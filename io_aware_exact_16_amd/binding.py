@@ -22,7 +22,8 @@ FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
                 -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG"}
-EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_fwd_decode_workspace_bytes", "fa_fwd_decode",
+            "fa_lse_merge", "fa_status_string")
 BLOCK = 128   # tokens per FP8 scaling block
 
 
@@ -51,6 +52,12 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = I
     lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
     lib.fa_hadamard_fp8_quant.restype = I
+    lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.fa_fwd_decode.restype = I
+    lib.fa_lse_merge.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
+    lib.fa_lse_merge.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -135,6 +142,51 @@ def fa_hadamard_fp8_quant(x, x8, scales, hadamard: bool) -> None:
     _check("fa_hadamard_fp8_quant", st)
 
 
+def fa_fwd_decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    """Device workspace (bytes) fa_fwd_decode needs; 0 for invalid sizes.  No GPU needed."""
+    return int(load().fa_fwd_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
+
+
+def fa_fwd_decode(q, k, v, o, lse, scale: float, causal: bool, workspace) -> None:
+    """O, LSE <- attention of q [B,H,Nq,d] against k, v [B,H,Nk,d] (bf16), split over the keys.
+    Causal: the queries are the last Nq of the Nk tokens.  ``workspace``: a CUDA tensor of
+    at least fa_fwd_decode_workspace_bytes(...) bytes."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _dev4("q", q, torch.bfloat16)
+    _dev4("k", k, torch.bfloat16, (B, H, Nk, d))
+    _dev4("v", v, torch.bfloat16, (B, H, Nk, d))
+    _dev4("o", o, torch.bfloat16, (B, H, Nq, d))
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, Nq)):
+        raise ValueError("fa_fwd_decode: lse must be a contiguous float32 CUDA tensor [B,H,Nq]")
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("fa_fwd_decode: workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                              int(bool(causal)), _ptr(workspace), nbytes, _stream(q))
+    _check("fa_fwd_decode", st)
+
+
+def fa_lse_merge(o_parts, lse_parts, o, lse) -> None:
+    """O, LSE <- merge of P partial attentions: o_parts [P,B,H,N,d] and lse_parts [P,B,H,N]
+    (float32); o [B,H,N,d] float32 or bf16, lse [B,H,N] float32."""
+    code = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(o.dtype)
+    if code is None:
+        raise ValueError(f"fa_lse_merge: unsupported output dtype {o.dtype}")
+    if not (o_parts.is_cuda and o_parts.is_contiguous() and o_parts.dtype == torch.float32 and o_parts.dim() == 5):
+        raise ValueError("fa_lse_merge: o_parts must be a contiguous float32 CUDA tensor [P,B,H,N,d]")
+    P, B, H, N, d = o_parts.shape
+    if not (lse_parts.is_cuda and lse_parts.is_contiguous() and lse_parts.dtype == torch.float32
+            and tuple(lse_parts.shape) == (P, B, H, N)):
+        raise ValueError("fa_lse_merge: lse_parts must be a contiguous float32 CUDA tensor [P,B,H,N]")
+    _dev4("o", o, o.dtype, (B, H, N, d))
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("fa_lse_merge: lse must be a contiguous float32 CUDA tensor [B,H,N]")
+    st = load().fa_lse_merge(_ptr(o_parts), _ptr(lse_parts), P, B, H, N, d, _ptr(o), code, _ptr(lse),
+                             _stream(o_parts))
+    _check("fa_lse_merge", st)
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (torch allocates the outputs, the library computes)
 def attention(q, k, v, causal: bool = False, scale: float | None = None):
@@ -163,4 +215,26 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, s
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
     fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, scale, causal)
+    return o, lse
+
+
+def attention_decode(q, k, v, causal: bool = False, scale: float | None = None):
+    """Return (o bf16, lse fp32) for q [B,H,Nq,d] against k, v [B,H,Nk,d] (bf16, on the GPU);
+    the workspace is a torch allocation."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    B, H, Nq, d = q.shape
+    nbytes = fa_fwd_decode_workspace_bytes(B, H, Nq, k.shape[2], d)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_decode(q, k, v, o, lse, scale, causal, ws)
+    return o, lse
+
+
+def lse_merge(o_parts, lse_parts, out_dtype=torch.float32):
+    """Return (o, lse) merging partial attentions o_parts [P,B,H,N,d], lse_parts [P,B,H,N]."""
+    o = torch.empty(o_parts.shape[1:], dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty(o_parts.shape[1:4], dtype=torch.float32, device=o_parts.device)
+    fa_lse_merge(o_parts, lse_parts, o, lse)
     return o, lse

@@ -1,5 +1,5 @@
-// Device helpers shared by the two bf16 attention kernels (streaming and
-// persistent ping-pong): register layouts of the 32x32x16 bf16 matrix
+// Device helpers shared by the bf16 attention kernels (streaming, persistent
+// ping-pong and split-KV decode): register layouts of the 32x32x16 bf16 matrix
 // instruction, the swizzled LDS tile layout, the buffer-to-LDS DMA and the
 // half-wave reductions.  Included by HIP translation units only.
 //
@@ -75,6 +75,119 @@ template <int V>
 struct IC {
   static constexpr int value = V;
 };
+
+// One 64-key tile of one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+// kt / vt are the LDS K and V tiles; koff / voff are this lane's byte offsets
+// into them (first 32-key block, first 16-key chunk); MASK marks tiles that
+// cross the causal diagonal or the end of the sequence.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void tile_math(const char* kt, const char* vt, const uint32_t (&koff)[D / 16],
+                                          const uint32_t (&voff)[D / 32][2], const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&acc)[D / 32], float& m2, float& lsum, float c, int j0, int qi,
+                                          int N, int half) {
+  constexpr int KB_BYTES = 32 * D * 2;   // one 32-key block of the tile
+  constexpr int KC_BYTES = 16 * D * 2;   // one 16-key chunk of the tile
+  f32x16 s[BC / 32];
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[dc] + kb * KB_BYTES);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
+    }
+  // keep 8 K-operand reads in flight ahead of the matrix ops
+  constexpr int NMF = (D / 16) * (BC / 32);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < NMF - 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+
+  __builtin_amdgcn_sched_barrier(0);
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
+        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+      }
+  }
+
+  float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // 4 independent chains
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pm[(kb * 2 + (r >> 3)) & 3] = fmaxf(pm[(kb * 2 + (r >> 3)) & 3], s[kb][r]);
+  float tmax = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+  tmax = wave_halves_max(tmax);
+  const float tm2 = tmax * c;
+  if (__any(tm2 > m2 + RESCALE_THRESHOLD)) {
+    const float mnew = fmaxf(m2, tm2);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    lsum *= alpha;
+    m2 = mnew;
+  }
+
+  // p = exp2(c s - m2), rounded to bf16 as the B operand of P V; the row sum
+  // uses the float32 p (summing the bf16-rounded values would cost up to 2^-9
+  // relative in l, i.e. in LSE, on rows with few keys).  P of chunk kc+1 is
+  // computed while the matrix ops of chunk kc run.
+  bf16x8 pb[BC / 16];
+  float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto pchunk = [&](int kc) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float s0 = s[kc >> 1][8 * (kc & 1) + e], s1 = s[kc >> 1][8 * (kc & 1) + e + 1];
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m2));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m2));
+      if (MASK) {                        // exact zeros for masked keys, also when c = 0
+        p0 = s0 == -INFINITY ? 0.0f : p0;
+        p1 = s1 == -INFINITY ? 0.0f : p1;
+      }
+      rs[e >> 1] += p0 + p1;
+      pb[kc][e] = (__bf16)p0;
+      pb[kc][e + 1] = (__bf16)p1;
+    }
+  };
+  pchunk(0);
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16x4_t v0 = tr_read(vt + voff[db][0] + kc * KC_BYTES);
+      const bf16x4_t v1 = tr_read(vt + voff[db][1] + kc * KC_BYTES);
+      const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], acc[db], 0, 0, 0);
+    }
+    if (kc + 1 < BC / 16) pchunk(kc + 1);
+  }
+  lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  // schedule: P chunk 0, then per chunk: its 8 transposed V reads, and its 4
+  // matrix ops each followed by a quarter of the next chunk's VALU work
+  constexpr int VPC = MASK ? 28 : 20;      // VALU instructions per P chunk
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 1);
+  __builtin_amdgcn_sched_group_barrier(0x002, VPC, 1);
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc) {
+    if (kc + 1 < BC / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (kc + 1 < BC / 16) __builtin_amdgcn_sched_group_barrier(0x002, VPC / (D / 32), 1);
+    }
+  }
+}
 
 }  // namespace bf16k
 }  // namespace fa

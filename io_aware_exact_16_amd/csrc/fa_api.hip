@@ -1,6 +1,7 @@
 // C entry points of libfa.so: argument checks, kernel-instance dispatch, launch
 // on the caller's stream.  Declared and documented in include/fa.h.
 #include <math.h>
+#include <stddef.h>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
@@ -71,6 +72,55 @@ int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scale
                                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_fwd_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+  if (!sizes_ok(B, H, Nq, d, 1) || !sizes_ok(B, H, Nk, d, 1)) return 0;
+  int S = 0, chunk = 0;
+  fa::decode_split(B, H, Nq, Nk, &S, &chunk);
+  return (size_t)S * B * H * Nq * (size_t)(d + 1) * sizeof(float);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, Nq, d, 32) || !sizes_ok(B, H, Nk, d, 64)) return FA_ERR_SHAPE;
+  if ((long long)Nk * d * 4 >= (1LL << 32) || (long long)Nq * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;
+  if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;   // the queries are the last Nq of the Nk tokens
+  int S = 0, chunk = 0;
+  fa::decode_split(B, H, Nq, Nk, &S, &chunk);
+  const long long units = (long long)S * B * H * ((Nq + 31) / 32);
+  if (units > kMaxGrid || (long long)B * H * Nq > kMaxGrid) return FA_ERR_SHAPE;
+  const size_t need = (size_t)S * B * H * Nq * (size_t)(d + 1) * sizeof(float);
+  if (workspace_bytes < need) return FA_ERR_ARG;
+  const void* ins[3] = {q, k, v};
+  for (const void* p : ins)
+    if (p == o || p == (const void*)lse || p == (const void*)workspace) return FA_ERR_ARG;
+  if ((void*)lse == o || workspace == o || workspace == (void*)lse) return FA_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* op = static_cast<float*>(workspace);
+  float* lp = op + (size_t)S * B * H * Nq * d;
+  hipError_t e = fa::launch_attn_decode_bf16(q, k, v, op, lp, B, H, Nq, Nk, d, scale, causal != 0, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  return launch_status(fa::launch_lse_merge(op, lp, o, true, lse, S, (long)B * H * Nq, d, s));
+}
+
+int fa_lse_merge(const float* o_parts, const float* lse_parts, int P, int B, int H, int N, int d, void* o,
+                 int o_dtype, float* lse, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (P < 1 || !sizes_ok(B, H, N, d, 1)) return FA_ERR_SHAPE;
+  if ((long double)P * B * H * N * d >= 9.0e18L) return FA_ERR_SHAPE;
+  const void* ins[2] = {o_parts, lse_parts};
+  for (const void* p : ins)
+    if (p == o || p == (const void*)lse) return FA_ERR_ARG;
+  if ((void*)lse == o) return FA_ERR_ARG;
+  return launch_status(fa::launch_lse_merge(o_parts, lse_parts, o, o_dtype == FA_BF16, lse, P, (long)B * H * N, d,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -79,7 +129,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_DTYPE: return "unknown or unsupported dtype for this entry point";
     case FA_ERR_UNSUPPORTED: return "head dimension not supported for this entry point";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "invalid argument: non-finite scale, flag not 0/1, or output aliasing an input";
+    case FA_ERR_ARG:
+      return "invalid argument: non-finite scale, flag not 0/1, an output aliasing an input, or a workspace too small";
     default: return "unknown status";
   }
 }

@@ -14,6 +14,18 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
 hipError_t launch_attn_bf16_pp(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int N, float scale, hipStream_t stream);
 
+// Split-KV decode: how the Nk keys are cut into S chunks of `chunk` keys (a
+// pure function of the sizes, shared by the launcher and the workspace query).
+void decode_split(int B, int H, int Nq, int Nk, int* S, int* chunk);
+
+// Partial results of every chunk: op [S, B*H, Nq, d] float32, lp [S, B*H, Nq].
+hipError_t launch_attn_decode_bf16(const void* q, const void* k, const void* v, float* op, float* lp, int B, int H,
+                                   int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
+
+// Merge P parts [P, rows, d] / [P, rows] into o [rows, d] (bf16 or float32) and lse [rows].
+hipError_t launch_lse_merge(const float* op, const float* lp, void* o, bool bf16_out, float* lse, int P, long rows,
+                            int d, hipStream_t stream);
+
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
 

@@ -35,24 +35,40 @@ class Workload:
     std: float = 1.0
     outlier_frac: float = 0.0
     outlier_value: float = 20.0
+    n_q: int = 0            # decode shape: n_q queries (the last n_q of N tokens) against N keys; 0 = N queries
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     @property
+    def nq(self) -> int:
+        return self.n_q if self.n_q > 0 else self.N
+
+    @property
     def flops(self) -> float:
-        """Attention FLOPs counted the usual way: 4*B*H*N^2*d, halved when causal."""
+        """Attention FLOPs counted the usual way: 4*B*H*N^2*d, halved when causal.  For a
+        decode shape: 4*d per visible (query, key) pair."""
+        if self.n_q > 0:
+            pairs = self.n_q * self.N - (self.n_q * (self.n_q - 1) // 2 if self.causal else 0)
+            return 4.0 * self.B * self.H * pairs * self.d
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if self.causal else f
+
+    @property
+    def hbm_bytes(self) -> float:
+        """Algorithmic HBM traffic of one forward: Q, K, V read once, O and LSE written once."""
+        es = 4 if self.dtype == "f32" else 2
+        return float(self.B * self.H * ((2 * self.N + 2 * self.nq) * self.d * es + 4 * self.nq))
 
     def with_shape(self, **kw) -> "Workload":
         return replace(self, **kw)
 
 
 # The workloads: a tiny fp32 case, bf16 causal and non-causal cases, the FP8
-# causal case with outliers, its bf16 twin at the same 8k shape, and a
-# 32k-token layer shaped like a 7B model's attention (32 heads of 128).
+# causal case with outliers, its bf16 twin at the same 8k shape, a 32k-token
+# layer shaped like a 7B model's attention (32 heads of 128), and one decode
+# step (one new token per sequence) against that layer's 32k-token keys.
 WORKLOADS = {
     "f32_tiny": Workload("f32_tiny", 1, 1, 128, 64, False, "f32", seed=1001),
     "bf16_causal_2k": Workload("bf16_causal_2k", 4, 16, 2048, 128, True, "bf16", seed=1002),
@@ -61,6 +77,8 @@ WORKLOADS = {
                               outlier_frac=0.001, outlier_value=20.0),
     "bf16_causal_8k": Workload("bf16_causal_8k", 2, 16, 8192, 128, True, "bf16", seed=1006),
     "bf16_causal_32k": Workload("bf16_causal_32k", 1, 32, 32768, 128, True, "bf16", seed=1005, std=0.5),
+    # one decode step of four 32k-token sequences through the 7B-shaped layer
+    "bf16_decode_32k": Workload("bf16_decode_32k", 4, 32, 32768, 128, True, "bf16", seed=1007, n_q=1),
 }
 
 # The 8k-token causal bf16 workload is the headline throughput point.
@@ -74,7 +92,7 @@ def _outliers(x: torch.Tensor, g: torch.Generator, frac: float, value: float) ->
 
 
 def make_qkv(w: Workload, seed: int | None = None):
-    """Return (q, k, v) as contiguous CPU tensors of shape [B, H, N, d].
+    """Return (q, k, v) as contiguous CPU tensors: q [B, H, nq, d], k and v [B, H, N, d].
 
     dtype float32 for the fp32 workload, bfloat16 otherwise (the FP8 workload's
     tensors are the bf16 source values that the quantiser reads).
@@ -82,7 +100,7 @@ def make_qkv(w: Workload, seed: int | None = None):
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else seed)
     shape = (w.B, w.H, w.N, w.d)
-    q = torch.randn(shape, generator=g, dtype=torch.float32) * w.std
+    q = torch.randn((w.B, w.H, w.nq, w.d), generator=g, dtype=torch.float32) * w.std
     k = torch.randn(shape, generator=g, dtype=torch.float32) * w.std
     v = torch.randn(shape, generator=g, dtype=torch.float32) * w.std
     if w.outlier_frac > 0.0:
@@ -94,7 +112,7 @@ def make_qkv(w: Workload, seed: int | None = None):
 
 
 def custom(B: int, H: int, N: int, d: int, causal: bool, dtype: str = "bf16", seed: int = 7,
-           std: float = 1.0, outlier_frac: float = 0.0) -> Workload:
+           std: float = 1.0, outlier_frac: float = 0.0, n_q: int = 0) -> Workload:
     """An ad-hoc workload (edge shapes in tests) drawn by the same recipe."""
     return Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, causal, dtype, seed=seed, std=std,
-                    outlier_frac=outlier_frac)
+                    outlier_frac=outlier_frac, n_q=n_q)

@@ -20,7 +20,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_status_string"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8",
+                                    "fa_hadamard_fp8_quant", "fa_lse_merge", "fa_status_string"]
 
 
 @pytest.fixture(scope="module")
@@ -87,6 +88,10 @@ def _sig(lib):
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, P]
     lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
     lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.fa_lse_merge.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
 
 
 @pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
@@ -120,3 +125,46 @@ def test_quant_validation(lib):
     assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 0, 128, 1, None) == -2
     assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 8, 128, 3, None) == -6
     assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE, FAKE3, 1, 1, 8, 128, 1, None) == -6
+
+
+def test_decode_workspace_bytes(lib):
+    """Host-only size query: a whole number of key chunks of at least 256 keys each
+    (fewer only when Nk < 256), and 0 for invalid sizes."""
+    _sig(lib)
+    ws = lib.fa_fwd_decode_workspace_bytes
+    for bad in [(0, 1, 1, 8, 128), (1, 1, 0, 8, 128), (1, 1, 1, 0, 128), (1, 1, 1, 8, 96)]:
+        assert ws(*bad) == 0
+    for (B, H, Nq, Nk, d) in [(1, 1, 1, 1, 128), (1, 1, 1, 200, 64), (4, 32, 1, 32768, 128), (2, 8, 40, 5000, 128),
+                              (1, 32, 7, 131072, 64), (64, 64, 33, 4096, 128)]:
+        n = ws(B, H, Nq, Nk, d)
+        per_split = B * H * Nq * (d + 1) * 4
+        assert n > 0 and n % per_split == 0, (B, H, Nq, Nk, d, n)
+        S = n // per_split
+        assert 1 <= S <= max(1, -(-Nk // 256)), (B, H, Nq, Nk, d, S)
+        if B * H * (-(-Nq // 32)) >= 2048:
+            assert S == 1
+    assert ws(4, 32, 1, 32768, 128) == 16 * 4 * 32 * 129 * 4     # 16 chunks of 2048 keys
+
+
+@pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
+def test_decode_and_merge_validation(lib):
+    _sig(lib)
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)]
+    big = 1 << 30
+    dec = lib.fa_fwd_decode
+    assert dec(*p[:5], 1, 1, 1, 64, 128, 0.1, 1, NULL, big, None) == -1              # no workspace
+    assert dec(*p[:5], 1, 1, 1, 64, 96, 0.1, 1, p[5], big, None) == -4
+    assert dec(*p[:5], 1, 1, 65, 64, 128, 0.1, 1, p[5], big, None) == -2             # causal needs Nq <= Nk
+    assert dec(*p[:5], 1, 1, 0, 64, 128, 0.1, 0, p[5], big, None) == -2
+    assert dec(*p[:5], 1, 1, 1, 64, 128, float("nan"), 0, p[5], big, None) == -6
+    assert dec(*p[:5], 1, 1, 1, 64, 128, 0.1, 3, p[5], big, None) == -6
+    assert dec(*p[:5], 1, 1, 1, 64, 128, 0.1, 1, p[5], 16, None) == -6               # workspace too small
+    assert dec(*p[:5], 1, 1, 1, 64, 128, 0.1, 1, p[0], big, None) == -6              # workspace aliases q
+    assert dec(p[0], p[1], p[2], p[0], p[4], 1, 1, 1, 64, 128, 0.1, 1, p[5], big, None) == -6   # o aliases q
+    mrg = lib.fa_lse_merge
+    assert mrg(NULL, p[1], 2, 1, 1, 8, 128, p[2], 0, p[3], None) == -1
+    assert mrg(p[0], p[1], 2, 1, 1, 8, 128, p[2], 2, p[3], None) == -3              # FP8 output: no
+    assert mrg(p[0], p[1], 2, 1, 1, 8, 96, p[2], 0, p[3], None) == -4
+    assert mrg(p[0], p[1], 0, 1, 1, 8, 128, p[2], 0, p[3], None) == -2              # no part
+    assert mrg(p[0], p[1], 2, 1, 1, 8, 128, p[0], 0, p[3], None) == -6              # o aliases o_parts
+    assert mrg(p[0], p[1], 2, 1, 1, 8, 128, p[2], 1, p[2], None) == -6              # lse aliases o
