@@ -6,12 +6,14 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 that is already resident in HBM: for the bf16/fp32 workloads one fa_fwd call;
 for the FP8 workload the three Hadamard/FP8 quantiser calls (Q and K with the
-transform, V without) followed by fa_fwd_fp8.  W untimed steps, then K timed
+transform, V without) followed by fa_fwd_fp8; for the decode workload one
+fa_fwd_decode call (split-KV kernel + merge).  W untimed steps, then K timed
 steps bracketed by device synchronisation, timed with HIP events on the stream
 the kernels are launched on.  Prints ONE JSON line.
 
 Throughput counts attention FLOPs as 4*B*H*N^2*d (halved when causal) per
-step.  The roofline object reports the dominant kernel (the attention kernel)
+step; the decode workload, which is bound by reading K and V, reports its
+algorithmic HBM bytes per second against the 8 TB/s HBM peak instead.  The roofline object reports the dominant kernel (the attention kernel)
 against the MI355X dense matrix peak of its input type; "traffic" is the HBM
 byte count per launch measured with hardware counters (profiles/traffic.json),
 or null when that kernel's source changed since the counters were taken.
@@ -34,10 +36,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense, published
+PEAK_HBM_GBS = 8000.0                                         # MI355X HBM3E, published
 
 
 def kernel_source(w) -> str:
     """Source file of the attention kernel that runs this workload."""
+    if w.n_q > 0:
+        return "attn_decode.hip"
     if w.dtype == "bf16":
         return "attn_bf16_pp.hip" if (w.causal and w.d == 128) else "attn_bf16.hip"
     return {"fp8": "attn_fp8.hip", "f32": "attn_f32.hip"}[w.dtype]
@@ -86,16 +91,20 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     vn = v.float().numpy().astype(np.float64)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done, t_used = 0, 0.0
-    per_head = 4.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    decode = w.n_q > 0
+    per_head = (w.hbm_bytes if decode else w.flops) / len(heads)   # bytes (decode) or FLOPs per head
+    q_index = oracle.decode_positions(w.nq, w.N) if decode else None
     for (b, h) in heads:
         t0 = time.perf_counter()
-        oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], w.scale, w.causal)
+        oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], w.scale, w.causal,
+                         q_index=q_index)
         t_used += time.perf_counter() - t0
         done += 1
         if t_used >= budget_s:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": done * per_head / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    value = done * per_head / t_used / (1e9 if decode else 1e12)
+    return {"value": value, "unit": "GB/s" if decode else "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {len(heads)} (batch, head) pairs, full rows, float64, {t_used:.1f} s"}
 
 
@@ -149,6 +158,17 @@ def main() -> int:
             fa.fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, w.scale, w.causal)
             if record is not None:
                 record[1].record(stream)
+    elif w.n_q > 0:                           # decode step: split-KV kernel + merge, caller-owned workspace
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_fwd_decode_workspace_bytes(w.B, w.H, w.nq, w.N, w.d), dtype=torch.uint8, device=dev)
+
+        def step(record=None):
+            if record is not None:
+                record[0].record(stream)
+            fa.fa_fwd_decode(qd, kd, vd, o, lse, w.scale, w.causal, ws)
+            if record is not None:
+                record[1].record(stream)
     else:
         o = torch.empty_like(qd)
         lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
@@ -178,15 +198,20 @@ def main() -> int:
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     ms_per_step = total_ms / args.steps
 
-    flops = w.flops
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     dtype = w.dtype
-    peak = PEAK_TFLOPS[dtype]
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+    if w.n_q > 0:
+        # a decode step reads K and V once and does little arithmetic per byte: HBM-bound
+        metric = "decode attention fwd: algorithmic HBM GB/s (Q,K,V read once, O,LSE written once), 1 GPU"
+        unit, work, peak, bound = "GB/s", w.hbm_bytes / 1e9, PEAK_HBM_GBS, "hbm"
+    else:
+        metric = "attention fwd TFLOPS (4*B*H*N^2*d, x1/2 causal) and % of MFMA peak, 1 GPU"
+        unit, work, peak, bound = "TFLOP/s", w.flops / 1e12, PEAK_TFLOPS[dtype], "mfma"
+    value = work / (ms_per_step * 1e-3)
+    achieved = work / (kern_avg_ms * 1e-3)
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, kernel_source(w))}
-    eprint(f"[bench] {w.name}: step {ms_per_step:.4f} ms, attention kernel avg {kern_avg_ms:.4f} ms "
-           f"(min {min(kern_ms):.4f}), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} peak")
+    eprint(f"[bench] {w.name}: step {ms_per_step:.4f} ms, attention launch(es) avg {kern_avg_ms:.4f} ms "
+           f"(min {min(kern_ms):.4f}), {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of {peak} peak")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -195,11 +220,12 @@ def main() -> int:
         eprint(f"[bench] cpu_baseline: {cpu}")
 
     line = {
-        "metric": "attention fwd TFLOPS (4*B*H*N^2*d, x1/2 causal) and % of MFMA peak, 1 GPU",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "metric": metric,
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[dtype], "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   **({"Nq": w.nq} if w.n_q > 0 else {}),
                    "input_dist": f"iid N(0,{w.std}^2)" + (f", {w.outlier_frac:.1%} coords = +-{w.outlier_value:g}"
                                                          if w.outlier_frac else ""),
                    "seed": w.seed},

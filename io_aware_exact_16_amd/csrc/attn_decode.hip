@@ -158,16 +158,21 @@ __global__ __launch_bounds__(D) void lse_merge_kernel(const float* __restrict__ 
                                                       long rows) {
   const long row = blockIdx.x;
   const int t = threadIdx.x;
+  // two passes (maximum, then weighted sums), each unrolled so that one
+  // thread's loads of several parts are in flight together
   float m = -INFINITY;
+#pragma unroll 8
   for (int p = 0; p < P; ++p) m = fmaxf(m, LP[(long)p * rows + row]);
   float num = 0.0f, den = 0.0f;
   if (m > -INFINITY) {
+#pragma unroll 8
     for (int p = 0; p < P; ++p) {
       const float l = LP[(long)p * rows + row];
-      if (l == -INFINITY) continue;          // a part with no visible key (its O is not read)
+      const float op = OP[((long)p * rows + row) * D + t];
+      if (l == -INFINITY) continue;          // a part with no visible key: weight 0, its O ignored
       const float w = __expf(l - m);
       den += w;
-      num += w * OP[((long)p * rows + row) * D + t];
+      num += w * op;
     }
   }
   const float o = den > 0.0f ? num / den : 0.0f;
