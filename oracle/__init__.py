@@ -10,6 +10,8 @@ nothing here imports them: the two implementations share no code.
   merge.lse_merge      -- combine partial attentions over disjoint key sets
                           through their LSEs; merge.decode_positions gives the
                           query positions of a decode step
+  backward.attention_bwd -- dQ, dK, dV of the attention definition for an
+                          upstream gradient dO (chain rule, full rows)
   fp8.*                -- Sylvester Hadamard matrix, E4M3 encode/decode from
                           the bit layout, per-block quantisation, and attention
                           on dequantised FP8 operands
@@ -19,8 +21,9 @@ brute force and library routines; none is marked "parity unpinned".
 """
 from .attention import attention
 from .merge import lse_merge, decode_positions
+from .backward import attention_bwd
 from .fp8 import (sylvester_hadamard, orthonormal_hadamard, e4m3_decode, e4m3_encode,
                   quantize_blocks, dequantize_blocks, attention_fp8, E4M3_MAX, BLOCK)
 
-__all__ = ["attention", "lse_merge", "decode_positions", "sylvester_hadamard", "orthonormal_hadamard", "e4m3_decode", "e4m3_encode",
+__all__ = ["attention", "attention_bwd", "lse_merge", "decode_positions", "sylvester_hadamard", "orthonormal_hadamard", "e4m3_decode", "e4m3_encode",
            "quantize_blocks", "dequantize_blocks", "attention_fp8", "E4M3_MAX", "BLOCK"]

@@ -235,6 +235,80 @@ def test_matches_torch_sdpa_fp64(N, causal):
 
 
 # ---------------------------------------------------------------------------
+# Gradients (oracle.attention_bwd): pinned to finite differences of the pinned
+# forward, to torch autograd, and to identities of the softmax Jacobian.
+def _loss(q, k, v, do, scale, causal):
+    o, _ = attention(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_matches_central_differences(causal):
+    # every element of dQ, dK, dV against a central difference of L = sum(dO * O)
+    N, d, h, scale = 5, 3, 1e-5, 0.7
+    q, k, v, do = (rng.standard_normal((1, 2, N, d)) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal)
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = _loss(q, k, v, do, scale, causal)
+            x[idx] = x0 - h
+            lm = _loss(q, k, v, do, scale, causal)
+            x[idx] = x0
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, fd, atol=1e-8, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 130])
+def test_bwd_matches_torch_autograd_fp64(N, causal):
+    d = 32
+    gen = torch.Generator().manual_seed(100 + N)
+    q, k, v, do = (torch.randn(2, 2, N, d, dtype=torch.float64, generator=gen) for _ in range(4))
+    qt, kt, vt = (t.clone().requires_grad_(True) for t in (q, k, v))
+    s = 0.3 * (qt @ kt.transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    (torch.softmax(s, dim=-1) @ vt).backward(do)
+    dq, dk, dv = oracle.attention_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy(), 0.3, causal, row_band=7)
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_identities(causal):
+    # rows of P sum to one: sum_j dV_j = sum_i dO_i; rows of dS sum to zero:
+    # sum_j dK_j = 0; S is bilinear: <Q, dQ> = <K, dK> = sum_ij dS_ij S_ij
+    N, d = 40, 16
+    q, k, v, do = (rng.standard_normal((2, 3, N, d)) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.45, causal)
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose((q * dq).sum(axis=(2, 3)), (k * dk).sum(axis=(2, 3)), atol=1e-11)
+
+
+def test_bwd_special_cases():
+    d = 8
+    q, k, v, do = (rng.standard_normal((1, 1, 1, d)) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.9, False)      # one token: O = v
+    np.testing.assert_allclose(dv, do, atol=1e-15)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    N = 9                                                            # scale 0: P = 1/N
+    q, k, v, do = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.0, False)
+    np.testing.assert_allclose(dv, np.broadcast_to(do.mean(axis=2, keepdims=True), dv.shape), atol=1e-15)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.5, True)        # causal ends
+    assert np.all(dq[0, 0, 0] == 0)                                  # query 0 sees key 0 only
+    _, lse = attention(q, k, v, 0.5, True)
+    p_last = math.exp(0.5 * float(q[0, 0, -1] @ k[0, 0, -1]) - lse[0, 0, -1])
+    np.testing.assert_allclose(dv[0, 0, -1], p_last * do[0, 0, -1], atol=1e-14)   # key N-1: query N-1 only
+
+
+# ---------------------------------------------------------------------------
 # Hadamard
 def test_hadamard_matches_textbook_order8():
     rows = [l.split() for l in open(os.path.join(GOLDEN, "hadamard8.txt")) if not l.startswith("#") and l.strip()]
