@@ -7,14 +7,19 @@ A step is one pass of the whole hot path over one batch of synthetic input
 that is already resident in HBM: for the bf16/fp32 workloads one fa_fwd call;
 for the FP8 workload the three Hadamard/FP8 quantiser calls (Q and K with the
 transform, V without) followed by fa_fwd_fp8; for the decode workload one
-fa_fwd_decode call (split-KV kernel + merge).  W untimed steps, then K timed
+fa_fwd_decode call (split-KV kernel + merge); for the backward workload one
+fa_bwd call (Delta pass, dK/dV kernel, dQ kernel), with the forward's O and
+LSE computed once beforehand.  W untimed steps, then K timed
 steps bracketed by device synchronisation, timed with HIP events on the stream
 the kernels are launched on.  Prints ONE JSON line.
 
 Throughput counts attention FLOPs as 4*B*H*N^2*d (halved when causal) per
 step; the decode workload, which is bound by reading K and V, reports its
-algorithmic HBM bytes per second against the 8 TB/s HBM peak instead.  The roofline object reports the dominant kernel (the attention kernel)
-against the MI355X dense matrix peak of its input type; "traffic" is the HBM
+algorithmic HBM bytes per second against the 8 TB/s HBM peak instead; the
+backward workload counts the usual 2.5 times the forward's FLOPs (five
+products of the forward's size).  The roofline object reports the dominant
+kernel (the attention kernel; for the backward, its whole three-kernel
+launch sequence) against the MI355X dense matrix peak of its input type; "traffic" is the HBM
 byte count per launch measured with hardware counters (profiles/traffic.json),
 or null when that kernel's source changed since the counters were taken.
 The cpu_baseline object times the float64 CPU oracle on a bounded sample of
@@ -41,6 +46,8 @@ PEAK_HBM_GBS = 8000.0                                         # MI355X HBM3E, pu
 
 def kernel_source(w) -> str:
     """Source file of the attention kernel that runs this workload."""
+    if w.backward:
+        return "attn_bwd.hip"
     if w.n_q > 0:
         return "attn_decode.hip"
     if w.dtype == "bf16":
@@ -81,8 +88,9 @@ def copy_calibration(steps: int) -> None:
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": steps}))
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """Time the float64 oracle on whole heads of the workload until about budget_s."""
+def cpu_baseline(w, q, k, v, budget_s: float, do=None):
+    """Time the float64 oracle on whole heads of the workload until about budget_s
+    (for the backward workload: oracle.attention_bwd with the upstream gradient do)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import oracle
@@ -94,10 +102,15 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     decode = w.n_q > 0
     per_head = (w.hbm_bytes if decode else w.flops) / len(heads)   # bytes (decode) or FLOPs per head
     q_index = oracle.decode_positions(w.nq, w.N) if decode else None
+    don = do.float().numpy().astype(np.float64) if do is not None else None
     for (b, h) in heads:
         t0 = time.perf_counter()
-        oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], w.scale, w.causal,
-                         q_index=q_index)
+        if don is not None:
+            oracle.attention_bwd(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1],
+                                 don[b:b + 1, h:h + 1], w.scale, w.causal)
+        else:
+            oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], w.scale, w.causal,
+                             q_index=q_index)
         t_used += time.perf_counter() - t0
         done += 1
         if t_used >= budget_s:
@@ -133,7 +146,7 @@ def main() -> int:
         return 0
 
     import io_aware_exact_16_amd as fa
-    from io_aware_exact_16_amd.workloads import HEADLINE, WORKLOADS, make_qkv
+    from io_aware_exact_16_amd.workloads import HEADLINE, WORKLOADS, make_dout, make_qkv
 
     w = WORKLOADS[args.workload or HEADLINE]
     q, k, v = make_qkv(w)
@@ -156,6 +169,21 @@ def main() -> int:
             if record is not None:
                 record[0].record(stream)
             fa.fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, w.scale, w.causal)
+            if record is not None:
+                record[1].record(stream)
+    elif w.backward:                          # backward step: fa_bwd on the forward's O and LSE
+        do = make_dout(w)
+        dod = do.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        fa.fa_fwd(qd, kd, vd, o, lse, w.scale, w.causal)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+
+        def step(record=None):
+            if record is not None:
+                record[0].record(stream)
+            fa.fa_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, w.scale, w.causal, ws)
             if record is not None:
                 record[1].record(stream)
     elif w.n_q > 0:                           # decode step: split-KV kernel + merge, caller-owned workspace
@@ -203,6 +231,9 @@ def main() -> int:
         # a decode step reads K and V once and does little arithmetic per byte: HBM-bound
         metric = "decode attention fwd: algorithmic HBM GB/s (Q,K,V read once, O,LSE written once), 1 GPU"
         unit, work, peak, bound = "GB/s", w.hbm_bytes / 1e9, PEAK_HBM_GBS, "hbm"
+    elif w.backward:
+        metric = "attention bwd TFLOPS (10*B*H*N^2*d, x1/2 causal: dQ, dK, dV) and % of MFMA peak, 1 GPU"
+        unit, work, peak, bound = "TFLOP/s", w.flops / 1e12, PEAK_TFLOPS[dtype], "mfma"
     else:
         metric = "attention fwd TFLOPS (4*B*H*N^2*d, x1/2 causal) and % of MFMA peak, 1 GPU"
         unit, work, peak, bound = "TFLOP/s", w.flops / 1e12, PEAK_TFLOPS[dtype], "mfma"
@@ -216,7 +247,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         eprint("[bench] timing the CPU oracle on a sample of the workload ...")
-        cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
+        cpu = cpu_baseline(w, q, k, v, args.cpu_budget, do=do if w.backward else None)
         eprint(f"[bench] cpu_baseline: {cpu}")
 
     line = {
@@ -226,6 +257,7 @@ def main() -> int:
         "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[dtype], "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    **({"Nq": w.nq} if w.n_q > 0 else {}),
+                   **({"pass": "backward", "dout_dist": "iid N(0,1)"} if w.backward else {}),
                    "input_dist": f"iid N(0,{w.std}^2)" + (f", {w.outlier_frac:.1%} coords = +-{w.outlier_value:g}"
                                                          if w.outlier_frac else ""),
                    "seed": w.seed},

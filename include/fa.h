@@ -33,7 +33,7 @@
  *             Results are valid once the caller has synchronised that stream.
  *   Memory:   the library allocates nothing and keeps no mutable global state;
  *             concurrent calls from several host threads are safe (fa_fwd_decode
- *             takes its scratch space from the caller).
+ *             and fa_bwd take their scratch space from the caller).
  *   Errors:   arguments are checked before any HIP call.  On a negative status
  *             nothing has been enqueued and the outputs are untouched, except
  *             FA_ERR_LAUNCH, which reports a failed kernel launch.  Device
@@ -165,6 +165,38 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
  */
 int fa_lse_merge(const float* o_parts, const float* lse_parts, int P, int B, int H, int N, int d,
                  void* o, int o_dtype, float* lse, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for these sizes
+ * (0 when the sizes are invalid).  Host-only; no HIP call.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- backward pass of fa_fwd (bfloat16): the gradients of
+ * L = sum(dO * O) with respect to Q, K and V.  The pages motivate the method
+ * by the training of large models ("FlashAttention-3 (PT)", introduction and
+ * section "Desempenho e importancia"; "Flash Attention" glossary page, third
+ * paragraph) but print no formula for this pass; it is the chain rule
+ * through the definition above, with P = exp(scale Q K^T - LSE) recomputed
+ * tile by tile from the saved LSE (no N x N matrix in memory):
+ *     dV = P^T dO,  dS = P * (dO V^T - Delta),  Delta_i = dO_i . O_i,
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, o, dout : [B,H,N,d] bfloat16; o and lse as returned by fa_fwd for
+ *                      the same q, k, v, scale and causal flag.
+ *   lse              : [B,H,N] float32 (natural-log units).
+ *   dq, dk, dv       : [B,H,N,d] bfloat16 outputs, written in full.
+ *   d in {64, 128}; dtype must be FA_BF16 (FA_ERR_DTYPE otherwise).
+ *   workspace        : device memory owned by the caller, at least
+ *                      fa_bwd_workspace_bytes(B,H,N,d) bytes (FA_ERR_ARG
+ *                      otherwise); it receives Delta and LSE log2(e), float32
+ *                      [B,H,N] each.  Calls that share a workspace must not run
+ *                      concurrently.
+ * Three kernels on `stream`; the results are deterministic (no atomics).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

@@ -23,7 +23,7 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
                 -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG"}
 EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_fwd_decode_workspace_bytes", "fa_fwd_decode",
-            "fa_lse_merge", "fa_status_string")
+            "fa_lse_merge", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string")
 BLOCK = 128   # tokens per FP8 scaling block
 
 
@@ -58,6 +58,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_decode.restype = I
     lib.fa_lse_merge.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
     lib.fa_lse_merge.restype = I
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, ctypes.c_size_t, P]
+    lib.fa_bwd.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -187,6 +191,28 @@ def fa_lse_merge(o_parts, lse_parts, o, lse) -> None:
     _check("fa_lse_merge", st)
 
 
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    """Device workspace (bytes) fa_bwd needs; 0 for invalid sizes.  No GPU needed."""
+    return int(load().fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, workspace) -> None:
+    """dQ, dK, dV <- gradients of sum(dout * O) for O, LSE = attention(q, k, v); all
+    [B,H,N,d] bf16 except lse [B,H,N] float32.  ``workspace``: a CUDA tensor of at
+    least fa_bwd_workspace_bytes(...) bytes."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _dev4(name, t, torch.bfloat16, (B, H, N, d))
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("fa_bwd: lse must be a contiguous float32 CUDA tensor [B,H,N]")
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("fa_bwd: workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                       B, H, N, d, float(scale), int(bool(causal)), FA_BF16, _ptr(workspace), nbytes, _stream(q))
+    _check("fa_bwd", st)
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (torch allocates the outputs, the library computes)
 def attention(q, k, v, causal: bool = False, scale: float | None = None):
@@ -238,3 +264,15 @@ def lse_merge(o_parts, lse_parts, out_dtype=torch.float32):
     lse = torch.empty(o_parts.shape[1:4], dtype=torch.float32, device=o_parts.device)
     fa_lse_merge(o_parts, lse_parts, o, lse)
     return o, lse
+
+
+def attention_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None):
+    """Return (dq, dk, dv) bf16 for the forward (o, lse) = attention(q, k, v, causal, scale)
+    and the upstream gradient dout; the workspace is a torch allocation."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    B, H, N, d = q.shape
+    ws = torch.empty(max(fa_bwd_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, causal, ws)
+    return dq, dk, dv

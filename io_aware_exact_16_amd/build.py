@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "attn_bf16.hip", "attn_bf16_pp.hip", "attn_decode.hip", "attn_f32.hip", "attn_fp8.hip", "hadamard_fp8.hip"]
+SOURCES = ["fa_api.hip", "attn_bf16.hip", "attn_bf16_pp.hip", "attn_decode.hip", "attn_bwd.hip", "attn_f32.hip", "attn_fp8.hip", "hadamard_fp8.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for every HIP translation unit.

@@ -49,11 +49,13 @@ __device__ __forceinline__ int key_of_arow(int m) {
 
 // 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
 // lds + 16 * i (lds must be the same for the whole wave).  The byte offset is
-// voffset (per lane) + soffset (per wave); reads past the buffer's byte size
-// return zeros.  (A plain device function: the builtin written inside a kernel
-// template keeps the host pass from emitting the kernel's launch stub.)
+// voffset (per lane) + soffset (per wave), both passed in the instruction's
+// per-lane offset, which the hardware checks against the buffer's byte size:
+// reads past it return zeros.  (A plain device function: the builtin written
+// inside a kernel template keeps the host pass from emitting the kernel's
+// launch stub.)
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset + soffset, 0, 0, 0);
 }
 
 __device__ __forceinline__ float wave_halves_max(float x) {

@@ -121,6 +121,33 @@ int fa_lse_merge(const float* o_parts, const float* lse_parts, int P, int B, int
                                             static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if ((d != 64 && d != 128) || !sizes_ok(B, H, N, d, 1)) return 0;
+  return fa::attn_bwd_workspace_bytes(B, H, N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, N, d, 16)) return FA_ERR_SHAPE;   // the Delta pass runs 16 rows per workgroup
+  if ((long long)N * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;   // same per-head limit as fa_fwd
+  if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (workspace_bytes < fa::attn_bwd_workspace_bytes(B, H, N)) return FA_ERR_ARG;
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  void* outs[4] = {dq, dk, dv, workspace};
+  for (void* w : outs)
+    for (const void* p : ins)
+      if (w == p) return FA_ERR_ARG;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[i] == outs[j]) return FA_ERR_ARG;
+  return launch_status(fa::launch_attn_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale,
+                                                causal != 0, static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -26,6 +26,13 @@ hipError_t launch_attn_decode_bf16(const void* q, const void* k, const void* v, 
 hipError_t launch_lse_merge(const float* op, const float* lp, void* o, bool bf16_out, float* lse, int P, long rows,
                             int d, hipStream_t stream);
 
+// Backward pass, bf16: workspace of attn_bwd_workspace_bytes(B, H, N) bytes
+// (LSE log2 e and Delta, float32 [B*H*N] each, 256-byte aligned).
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
+                                int d, float scale, bool causal, hipStream_t stream);
+
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
 

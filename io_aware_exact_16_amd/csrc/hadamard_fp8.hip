@@ -39,7 +39,7 @@ constexpr int BLK = 128;   // tokens per scaling block
 constexpr int EPT = 64;    // elements per thread
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset + soffset, 0, 0, 0);
 }
 
 template <int D, bool BF16IN>

@@ -12,7 +12,8 @@ Bernoulli mask for Q, the signs for Q, a Bernoulli mask for K and the signs
 for K.  Selected coordinates are replaced (not added to) by +-outlier_value.
 The float32 draws are finally rounded (round to nearest even) to bfloat16
 for every workload whose source precision is bf16; the fp32 workload keeps
-the float32 draws.
+the float32 draws.  A backward workload's upstream gradient dO comes from
+make_dout, a generator of its own.
 """
 from __future__ import annotations
 
@@ -36,6 +37,7 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_value: float = 20.0
     n_q: int = 0            # decode shape: n_q queries (the last n_q of N tokens) against N keys; 0 = N queries
+    backward: bool = False  # the workload is the backward pass (gradients for an upstream dO)
 
     @property
     def scale(self) -> float:
@@ -49,6 +51,8 @@ class Workload:
     def flops(self) -> float:
         """Attention FLOPs counted the usual way: 4*B*H*N^2*d, halved when causal.  For a
         decode shape: 4*d per visible (query, key) pair."""
+        if self.backward:         # five products of the forward's size instead of two
+            return 2.5 * self.with_shape(backward=False).flops
         if self.n_q > 0:
             pairs = self.n_q * self.N - (self.n_q * (self.n_q - 1) // 2 if self.causal else 0)
             return 4.0 * self.B * self.H * pairs * self.d
@@ -79,8 +83,9 @@ WORKLOADS = {
     "bf16_causal_32k": Workload("bf16_causal_32k", 1, 32, 32768, 128, True, "bf16", seed=1005, std=0.5),
     # one decode step of four 32k-token sequences through the 7B-shaped layer
     "bf16_decode_32k": Workload("bf16_decode_32k", 4, 32, 32768, 128, True, "bf16", seed=1007, n_q=1),
+    # the backward pass at the headline 8k shape (dO drawn by make_dout)
+    "bf16_causal_8k_bwd": Workload("bf16_causal_8k_bwd", 2, 16, 8192, 128, True, "bf16", seed=1008, backward=True),
 }
-
 # The 8k-token causal bf16 workload is the headline throughput point.
 HEADLINE = "bf16_causal_8k"
 
@@ -111,8 +116,18 @@ def make_qkv(w: Workload, seed: int | None = None):
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+def make_dout(w: Workload, seed: int | None = None):
+    """The upstream gradient dO for a backward workload: N(0, 1) of O's shape
+    [B, H, nq, d], rounded to bfloat16, from a generator of its own (seed + 7919)
+    so that Q, K, V are the same tensors make_qkv returns."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed((w.seed if seed is None else seed) + 7919)
+    do = torch.randn((w.B, w.H, w.nq, w.d), generator=g, dtype=torch.float32)
+    return do.to(torch.bfloat16).contiguous()
+
+
 def custom(B: int, H: int, N: int, d: int, causal: bool, dtype: str = "bf16", seed: int = 7,
-           std: float = 1.0, outlier_frac: float = 0.0, n_q: int = 0) -> Workload:
+           std: float = 1.0, outlier_frac: float = 0.0, n_q: int = 0, backward: bool = False) -> Workload:
     """An ad-hoc workload (edge shapes in tests) drawn by the same recipe."""
     return Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, causal, dtype, seed=seed, std=std,
-                    outlier_frac=outlier_frac, n_q=n_q)
+                    outlier_frac=outlier_frac, n_q=n_q, backward=backward)

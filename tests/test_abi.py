@@ -20,8 +20,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8",
-                                    "fa_hadamard_fp8_quant", "fa_lse_merge", "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
+                                    "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_hadamard_fp8_quant",
+                                    "fa_lse_merge", "fa_status_string"]
 
 
 @pytest.fixture(scope="module")
@@ -92,6 +93,9 @@ def _sig(lib):
     lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.fa_lse_merge.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, ctypes.c_size_t, P]
 
 
 @pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
@@ -168,3 +172,44 @@ def test_decode_and_merge_validation(lib):
     assert mrg(p[0], p[1], 0, 1, 1, 8, 128, p[2], 0, p[3], None) == -2              # no part
     assert mrg(p[0], p[1], 2, 1, 1, 8, 128, p[0], 0, p[3], None) == -6              # o aliases o_parts
     assert mrg(p[0], p[1], 2, 1, 1, 8, 128, p[2], 1, p[2], None) == -6              # lse aliases o
+
+
+def test_bwd_workspace_bytes(lib):
+    """Host-only size query: Delta and LSE log2(e), float32 [B,H,N] each, 256-byte aligned."""
+    _sig(lib)
+    ws = lib.fa_bwd_workspace_bytes
+    for bad in [(0, 1, 8, 128), (1, 0, 8, 128), (1, 1, 0, 128), (1, 1, 8, 96)]:
+        assert ws(*bad) == 0
+    for (B, H, N, d) in [(1, 1, 1, 128), (2, 16, 8192, 128), (3, 5, 1000, 64)]:
+        one = -(-(B * H * N * 4) // 256) * 256
+        assert ws(B, H, N, d) == 2 * one
+
+
+@pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
+def test_bwd_validation(lib):
+    _sig(lib)
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
+    big = 1 << 30
+    bwd = lib.fa_bwd
+
+    def call(ptrs=None, B=1, H=1, N=64, d=128, scale=0.1, causal=1, dtype=1, nbytes=big):
+        ptrs = p if ptrs is None else ptrs
+        return bwd(*ptrs[:9], B, H, N, d, scale, causal, dtype, ptrs[9], nbytes, None)
+
+    assert call(ptrs=p[:9] + [NULL]) == -1                      # no workspace
+    assert call(ptrs=[NULL] + p[1:]) == -1
+    assert call(dtype=0) == -3                                  # bf16 only
+    assert call(d=96) == -4
+    assert call(N=0) == -2
+    assert call(scale=float("inf")) == -6
+    assert call(causal=2) == -6
+    assert call(nbytes=16) == -6                                # workspace too small
+    q = list(p)
+    q[6] = q[0]                                                 # dq aliases q
+    assert call(ptrs=q) == -6
+    q = list(p)
+    q[8] = q[7]                                                 # dv aliases dk
+    assert call(ptrs=q) == -6
+    q = list(p)
+    q[9] = q[4]                                                 # workspace aliases lse
+    assert call(ptrs=q) == -6

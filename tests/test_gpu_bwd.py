@@ -1,0 +1,118 @@
+"""GPU parity of the backward pass (fa_bwd) against the fp64 oracle
+(oracle.attention_bwd) on seeded inputs: sequence lengths below one tile, at
+and around the 32-query / 64-key / 256-key tile edges and ragged, both head
+dimensions, causal and not, unusual scales, and the full-size backward
+workload on sampled heads.  The GPU forward supplies O and LSE, as a caller
+would; the oracle differentiates the definition from Q, K, V and dO alone.
+
+Tolerance, per gradient G in {dQ, dK, dV}, against the unrounded oracle on the
+same bf16-rounded inputs:
+    max |G - G_ref| <= 2e-2 * max|G_ref| + 1e-5   and   ||G - G_ref|| <= 1e-2 ||G_ref||
+(the second only where max|G_ref| > 1e-3).
+The arithmetic explains it: P and dS are rounded to bfloat16 (2^-9 relative)
+before the products that consume them, Delta comes from the bf16 forward output
+(2^-9 relative per element), and the gradients are stored in bfloat16 (2^-9
+relative); everything else is float32.  Each source costs at most about
+2^-9 = 2e-3 of the gradient's scale; the bars leave a factor of 5-10 over
+their sum, the same margin the forward's 2e-2 bar on O (entries of order 1)
+leaves.  The 1e-5 floor covers gradients that vanish exactly in real
+arithmetic but not in float32: with one key, dS = P (dO.V - dO.O) is zero by
+definition, while the two dot products are summed in different orders (a
+matrix instruction and the Delta pass) and differ by a few float32 ulps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_16_amd as fa
+import oracle
+from io_aware_exact_16_amd.workloads import WORKLOADS, custom, make_dout, make_qkv
+
+from gpu_helpers import f64, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, RMS_REL, ABS_FLOOR = 2e-2, 1e-2, 1e-5
+
+
+def _gpu_grads(q, k, v, do, causal, scale):
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _compare(name, g, ref, exact_zero=False):
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    if exact_zero:                      # dO = 0: every product is an exact zero
+        assert np.all(g == 0), f"{name}: expected exact zeros, max |G| = {float(np.abs(g).max()):.3g}"
+        return 0.0, 0.0
+    scale = float(np.abs(ref).max())
+    err = float(np.abs(g - ref).max())
+    assert err <= MAX_REL * scale + ABS_FLOOR, f"{name}: max |G - G_ref| = {err:.3g} > {MAX_REL} * {scale:.3g} + {ABS_FLOOR}"
+    if scale <= 1e-3:
+        return err, 0.0
+    rms = float(np.linalg.norm(g - ref)) / float(np.linalg.norm(ref))
+    assert rms <= RMS_REL, f"{name}: relative RMS error {rms:.3g} > {RMS_REL}"
+    return err / scale, rms
+
+
+def _check(B, H, N, d, causal, seed, scale=None, heads=None, dout_scale=1.0):
+    w = custom(B, H, N, d, causal, "bf16", seed=seed, backward=True)
+    scale = w.scale if scale is None else scale
+    q, k, v = make_qkv(w)
+    do = make_dout(w)
+    if dout_scale != 1.0:
+        do = (do.float() * dout_scale).to(torch.bfloat16)
+    log(f"[bwd] B={B} H={H} N={N} d={d} causal={causal} scale={scale:.4f} seed={seed}")
+    dq, dk, dv = (f64(t) for t in _gpu_grads(q, k, v, do, causal, scale))
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    qn, kn, vn, don = f64(q), f64(k), f64(v), f64(do)
+    worst = {}
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.attention_bwd(qn[sl], kn[sl], vn[sl], don[sl], scale, causal)
+        for name, g, r in (("dQ", dq[sl], rq), ("dK", dk[sl], rk), ("dV", dv[sl], rv)):
+            e = _compare(f"{name} head {(b, h)}", g, r, exact_zero=dout_scale == 0.0)
+            worst[name] = max(worst.get(name, (0, 0)), e)
+    log("  " + "  ".join(f"{n}: max/scale={e[0]:.3g} rms={e[1]:.3g}" for n, e in worst.items()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 32, 64, 100, 256, 257, 1000])
+def test_bwd_matches_oracle(gpu, N, d, causal):
+    _check(2, 3, N, d, causal, seed=N * 13 + d + int(causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_several_key_blocks(gpu, causal):
+    # 2100 keys: eight full 256-key blocks, one ragged, 66 query tiles
+    _check(1, 2, 2100, 128, causal, seed=2100 + int(causal))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
+def test_bwd_unusual_scales(gpu, scale):
+    _check(1, 2, 300, 128, True, seed=301, scale=scale)
+
+
+def test_bwd_zero_dout_gives_zero_gradients(gpu):
+    _check(1, 2, 130, 128, True, seed=302, dout_scale=0.0)
+
+
+def test_bwd_deterministic(gpu):
+    w = custom(1, 4, 777, 128, True, "bf16", seed=303, backward=True)
+    q, k, v = make_qkv(w)
+    do = make_dout(w)
+    a = _gpu_grads(q, k, v, do, True, w.scale)
+    b = _gpu_grads(q, k, v, do, True, w.scale)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_workload_sampled_heads(gpu):
+    # the full backward workload (2 x 16 heads of 8192 tokens, causal), in the
+    # launch configuration the benchmark times; two heads checked in full
+    w = WORKLOADS["bf16_causal_8k_bwd"]
+    _check(w.B, w.H, w.N, w.d, w.causal, seed=w.seed, heads=[(0, 0), (1, 15)])
