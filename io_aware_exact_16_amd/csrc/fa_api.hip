@@ -123,7 +123,7 @@ int fa_lse_merge(const float* o_parts, const float* lse_parts, int P, int B, int
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if ((d != 64 && d != 128) || !sizes_ok(B, H, N, d, 1)) return 0;
-  return fa::attn_bwd_workspace_bytes(B, H, N);
+  return fa::attn_bwd_workspace_bytes(B, H, N, d);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
@@ -135,7 +135,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!sizes_ok(B, H, N, d, 16)) return FA_ERR_SHAPE;   // the Delta pass runs 16 rows per workgroup
   if ((long long)N * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;   // same per-head limit as fa_fwd
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
-  if (workspace_bytes < fa::attn_bwd_workspace_bytes(B, H, N)) return FA_ERR_ARG;
+  if (workspace_bytes < fa::attn_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_ARG;
   const void* ins[6] = {q, k, v, o, lse, dout};
   void* outs[4] = {dq, dk, dv, workspace};
   for (void* w : outs)

@@ -175,14 +175,18 @@ def test_decode_and_merge_validation(lib):
 
 
 def test_bwd_workspace_bytes(lib):
-    """Host-only size query: Delta and LSE log2(e), float32 [B,H,N] each, 256-byte aligned."""
+    """Host-only size query: Delta and LSE log2(e), float32 [B,H,N] each, then d-major
+    bf16 copies of Q, dO and K in 64-token tiles [B,H,ceil(N/64),d,64], each part
+    256-byte aligned."""
     _sig(lib)
     ws = lib.fa_bwd_workspace_bytes
     for bad in [(0, 1, 8, 128), (1, 0, 8, 128), (1, 1, 0, 128), (1, 1, 8, 96)]:
         assert ws(*bad) == 0
+    up = lambda x: -(-x // 256) * 256
     for (B, H, N, d) in [(1, 1, 1, 128), (2, 16, 8192, 128), (3, 5, 1000, 64)]:
-        one = -(-(B * H * N * 4) // 256) * 256
-        assert ws(B, H, N, d) == 2 * one
+        f = up(B * H * N * 4)
+        t = up(B * H * -(-N // 64) * d * 64 * 2)
+        assert ws(B, H, N, d) == 2 * f + 3 * t
 
 
 @pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
