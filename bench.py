@@ -60,8 +60,22 @@ def eprint(*a):
 
 
 def source_sha(name: str) -> str:
-    with open(os.path.join(ROOT, "io_aware_exact_16_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of a kernel source together with the local headers it includes (recursively)."""
+    csrc = os.path.join(ROOT, "io_aware_exact_16_amd", "csrc")
+    h, seen, todo = hashlib.sha256(), set(), [os.path.join(csrc, name)]
+    while todo:
+        path = os.path.normpath(todo.pop(0))
+        if path in seen:
+            continue
+        seen.add(path)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(data)
+        for line in data.decode(errors="replace").splitlines():
+            line = line.strip()
+            if line.startswith('#include "'):
+                todo.append(os.path.join(os.path.dirname(path), line.split('"')[1]))
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str, kernel_src: str):
