@@ -7,9 +7,12 @@ workload.  It holds none of the attention or quantisation arithmetic, so both
 the CPU oracle's tests and the GPU path can take their inputs from it.
 
 Draw order for one workload (fixed, so every consumer sees identical tensors):
-Q, K, V from N(0, std^2) in float32; then, for the outlier workload only, a
-Bernoulli mask for Q, the signs for Q, a Bernoulli mask for K and the signs
-for K.  Selected coordinates are replaced (not added to) by +-outlier_value.
+Q, K, V from N(0, std^2) in float32; then, for the sparse-outlier workload
+only, a Bernoulli mask for Q, the signs for Q, a Bernoulli mask for K and the
+signs for K (selected coordinates are replaced, not added to, by
++-outlier_value); then, for the channel-outlier workload only, a random
+permutation of the d channels whose first channel_outliers entries are the
+channels multiplied by channel_scale in both Q and K.
 The float32 draws are finally rounded (round to nearest even) to bfloat16
 for every workload whose source precision is bf16; the fp32 workload keeps
 the float32 draws.  A backward workload's upstream gradient dO comes from
@@ -38,6 +41,8 @@ class Workload:
     outlier_value: float = 20.0
     n_q: int = 0            # decode shape: n_q queries (the last n_q of N tokens) against N keys; 0 = N queries
     backward: bool = False  # the workload is the backward pass (gradients for an upstream dO)
+    channel_outliers: int = 0     # Q and K: this many channels (the same for every token and head) scaled up
+    channel_scale: float = 1.0    # ... by this factor
 
     @property
     def scale(self) -> float:
@@ -83,6 +88,10 @@ WORKLOADS = {
     "bf16_causal_32k": Workload("bf16_causal_32k", 1, 32, 32768, 128, True, "bf16", seed=1005, std=0.5),
     # one decode step of four 32k-token sequences through the 7B-shaped layer
     "bf16_decode_32k": Workload("bf16_decode_32k", 4, 32, 32768, 128, True, "bf16", seed=1007, n_q=1),
+    # the FP8 case with structured outliers: 4 channels of Q and K (shared, as outlier features of a model's
+    # hidden state would be) carry 8x the standard deviation of the others
+    "fp8_channels_8k": Workload("fp8_channels_8k", 2, 16, 8192, 128, True, "fp8", seed=1009, channel_outliers=4,
+                                channel_scale=8.0),
     # the backward pass at the headline 8k shape (dO drawn by make_dout)
     "bf16_causal_8k_bwd": Workload("bf16_causal_8k_bwd", 2, 16, 8192, 128, True, "bf16", seed=1008, backward=True),
 }
@@ -111,6 +120,10 @@ def make_qkv(w: Workload, seed: int | None = None):
     if w.outlier_frac > 0.0:
         q = _outliers(q, g, w.outlier_frac, w.outlier_value)
         k = _outliers(k, g, w.outlier_frac, w.outlier_value)
+    if w.channel_outliers > 0:
+        ch = torch.randperm(w.d, generator=g)[:w.channel_outliers]
+        q[..., ch] *= w.channel_scale
+        k[..., ch] *= w.channel_scale
     if w.dtype in ("bf16", "fp8"):
         q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
     return q.contiguous(), k.contiguous(), v.contiguous()

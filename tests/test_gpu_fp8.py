@@ -137,3 +137,19 @@ def test_fp8_incoherent_processing_at_8k(gpu):
         pytest.xfail(f"Hadamard arm {errs[True]:.4f} >= plain FP8 {errs[False]:.4f} at 8192 tokens: with +-20 "
                      "outliers equal to the block maximum the plain arm quantises them exactly, and spreading them "
                      "costs more than it saves at this length (reproduced by the CPU emulation)")
+
+
+def test_fp8_incoherent_processing_on_channel_outliers(gpu):
+    """Structured outliers (4 channels of Q and K at 8x, the same in every token, 8192
+    tokens): the Hadamard arm lowers the error at least 2x (the pages report ~2.6x),
+    with a regression bound of 8e-2.  The 6e-2 bound, stated for the sparse-outlier
+    workload, is checked too and reported as an expected failure when exceeded."""
+    w = WORKLOADS["fp8_channels_8k"]
+    errs = _spec_errors(w, [(0, 0), (0, 7), (1, 3), (1, 15)], 256, 44)
+    log(f"[fp8_channels_8k] rel RMSE: no Hadamard {errs[False]:.4f}, Hadamard {errs[True]:.4f}, "
+        f"ratio {errs[False] / errs[True]:.2f}")
+    assert errs[False] >= 2.0 * errs[True]
+    assert errs[True] <= 8e-2
+    if errs[True] > 6e-2:
+        pytest.xfail(f"Hadamard arm {errs[True]:.4f} > 6e-2 at 8192 tokens (plain FP8 {errs[False]:.4f}): the "
+                     "error grows with the sequence length, as on the sparse-outlier workload")

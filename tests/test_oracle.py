@@ -519,6 +519,66 @@ def test_attention_fp8_p_quant_folds_v_block_scales():
     np.testing.assert_allclose(o[0, 0, i], num / p.sum(), rtol=0, atol=1e-12)
 
 
+def test_fp8_incoherent_processing_helps_on_channel_outliers():
+    # outlier *channels* shared by Q and K (the channel-outlier workload's model,
+    # at 1k tokens): the Hadamard transform spreads each outlier channel over all
+    # 128 coordinates of a row, and the pages' ~2.6x lower error appears
+    from io_aware_exact_16_amd.workloads import WORKLOADS, make_qkv
+    w = WORKLOADS["fp8_channels_8k"].with_shape(B=1, H=2, N=1024)
+    q, k, v = (t.double().numpy() for t in make_qkv(w))
+    o_ref, _ = attention(q, k, v, w.scale, True)
+    errs = {}
+    for had in (False, True):
+        q8, qs = oracle.quantize_blocks(q, had)
+        k8, ks = oracle.quantize_blocks(k, had)
+        v8, vs = oracle.quantize_blocks(v, False)
+        o, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, True)
+        errs[had] = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
+    assert errs[True] <= 6e-2 and errs[False] >= 2.0 * errs[True], errs
+
+
+def test_fp8_variants_study():
+    # Two FP8 variants measured in emulation (neither is built on the GPU): a
+    # Hadamard transform of V undone on O (O = (P (V H)) H, H symmetric and
+    # orthonormal), and MX-style power-of-two scales per 32 channels of a token.
+    # E4M3 is a floating format: per element its relative error does not depend
+    # on the scale (away from subnormals), and an orthogonal transform of V keeps
+    # the error energy of P V.  So neither variant lowers the error; the
+    # Hadamard transform of Q and K does, by spreading the products of shared
+    # outlier channels over all 128 terms of each dot product.
+    from oracle.fp8 import e4m3_decode, e4m3_encode, orthonormal_hadamard
+    N, d = 512, 128
+    g = np.random.default_rng(2024)
+    hm = orthonormal_hadamard(d)
+    bf = lambda x: torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    q_blk = lambda x: oracle.dequantize_blocks(*oracle.quantize_blocks(x, False))
+
+    def q_mx(x):
+        xr = x.reshape(x.shape[:-1] + (d // 32, 32))
+        amax = np.abs(xr).max(axis=-1, keepdims=True)
+        sc = np.where(amax > 0, 2.0 ** np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 1.0)
+        return (e4m3_decode(e4m3_encode(xr / sc)) * sc).reshape(x.shape)
+
+    q, k, v = (g.standard_normal((1, 2, N, d)) for _ in range(3))
+    ch = g.choice(d, 4, replace=False)
+    v[..., ch] *= 8.0
+    q, k, v = bf(q), bf(k), bf(v)
+    ref, _ = attention(q, k, v, d ** -0.5, True)
+    err = lambda o: np.linalg.norm(o - ref) / np.linalg.norm(ref)
+    e_v = err(attention(q, k, q_blk(v), d ** -0.5, True)[0])
+    e_hv = err(attention(q, k, q_blk(v @ hm), d ** -0.5, True)[0] @ hm)
+    e_mx = err(attention(q, k, q_mx(v), d ** -0.5, True)[0])
+    assert 0.9 * e_v <= e_hv and 0.9 * e_v <= e_mx, (e_v, e_hv, e_mx)      # no gain from either variant
+    q[..., ch] *= 8.0
+    k[..., ch] *= 8.0
+    q, k = bf(q), bf(k)
+    ref, _ = attention(q, k, v, d ** -0.5, True)
+    e_qk = err(attention(q_blk(q), q_blk(k), v, d ** -0.5, True)[0])
+    e_hqk = err(attention(q_blk(q @ hm), q_blk(k @ hm), v, d ** -0.5, True)[0])
+    e_mxqk = err(attention(q_mx(q), q_mx(k), v, d ** -0.5, True)[0])
+    assert e_qk >= 2.0 * e_hqk and e_mxqk >= 0.9 * e_qk, (e_qk, e_hqk, e_mxqk)
+
+
 def test_fp8_incoherent_processing_helps_at_1k_tokens():
     # outlier inputs as in the FP8 workload, at a short sequence where the
     # Hadamard arm is expected to have the lower error
