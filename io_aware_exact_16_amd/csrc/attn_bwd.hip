@@ -268,18 +268,23 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_kv_kernel(
     }
   };
 
+  // Query tiles are walked from the end of the sequence down, so that every
+  // workgroup of a head (each starting at its own first key when causal) reads
+  // the same tile at about the same time and the head's query-side data is
+  // fetched from HBM once, through the XCD's L2.
   const int qstart = CAUSAL ? k0 : 0;        // queries before the first key see none of these keys
   const int ntiles = (N - qstart + KV_TQ - 1) / KV_TQ;
+  const int qtop = qstart + (ntiles - 1) * KV_TQ;   // first query of the first tile walked
   const bool active = kw0 < N;
   const bool ktail = kw0 + KV_KW > N;
 
   auto step = [&](int t, const uint4* qc, const uint4* oc, const uint4* tc, const float* lc, const float* dlc,
                   uint4* qn, uint4* on, uint4* tn, float* ln, float* dn) {
-    const int q0 = qstart + t * KV_TQ;
+    const int q0 = qtop - t * KV_TQ;
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's part of tile t has landed
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's reads of the other buffers are done
     __asm__ volatile("s_barrier" ::: "memory");
-    if (t + 1 < ntiles) issue_tile(q0 + KV_TQ, qn, on, tn, ln, dn);
+    if (t + 1 < ntiles) issue_tile(q0 - KV_TQ, qn, on, tn, ln, dn);
     if (!active || (CAUSAL && q0 + KV_TQ - 1 < kw0)) return;   // no query of the tile sees these keys
     const char* qt = reinterpret_cast<const char*>(qc);
     const char* ot = reinterpret_cast<const char*>(oc);
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_kv_kernel(
     else tile(IC<0>{}, qt, ot, tt, lc, dlc, q0);
   };
 
-  issue_tile(qstart, qbuf0, obuf0, tbuf0, lbuf0, dbuf0);
+  issue_tile(qtop, qbuf0, obuf0, tbuf0, lbuf0, dbuf0);
   for (int t = 0; t < ntiles; t += 2) {
     step(t, qbuf0, obuf0, tbuf0, lbuf0, dbuf0, qbuf1, obuf1, tbuf1, lbuf1, dbuf1);
     if (t + 1 < ntiles) step(t + 1, qbuf1, obuf1, tbuf1, lbuf1, dbuf1, qbuf0, obuf0, tbuf0, lbuf0, dbuf0);
