@@ -193,7 +193,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                      [B,H,N] each, and d-major bf16 copies of Q, dO and K in
  *                      64-token tiles (about 3 B*H*N*d*2 bytes in all).  Calls
  *                      that share a workspace must not run concurrently.
- * Five kernels on `stream`; the results are deterministic (no atomics).
+ * Four kernels on `stream`; the results are deterministic (no atomics).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,

@@ -22,23 +22,20 @@
 //    less than half the byte rate.  All backward kernels stay clear of the
 //    LDS bandwidth limit this way (HBM cost: three bf16 copies, a few percent
 //    of the pass);
-//  * dV pass and dK pass (one kernel template): a workgroup of 8 waves (two
-//    per SIMD) owns 256 keys, 32 per wave, with K (and for dK, V) in
-//    registers as matrix-instruction operands; 32-query tiles of Q, dO, their
-//    d-major copies, LSE and Delta stream through LDS by DMA, double
-//    buffered.  Per tile: S = Q K^T, P; dV^T += dO^T P, or dP = dO V^T,
-//    dS = P (dP - Delta), dK^T += Q^T dS.  The two passes each recompute S:
-//    together they need the dK and dV accumulators, which do not fit with
-//    S and dP in one wave's registers at two waves per SIMD;
+//  * dK/dV pass: 4 waves (one per SIMD) own 128 keys, 32 each, with K and V in
+//    registers as B operands and the dK and dV accumulators in AGPRs; 32-query
+//    tiles of Q, dO, their d-major copies, LSE and Delta stream through LDS by
+//    DMA, double buffered.  Per tile: S = Q K^T, dP = dO V^T, P and dS, then
+//    dV^T += dO^T P and dK^T += Q^T dS.
 //  * dQ pass: 8 waves of 32 queries (Q and dO in registers), 64-key tiles of
 //    K, V and K's d-major copy through LDS; per tile S^T = K Q^T,
 //    dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 // The accumulator layout of the 32x32x16 instruction makes P and dS directly
 // the B operands of the products that consume them, as in the forward.  The
-// pass does 8 tile products instead of 5, and in exchange no workgroup ever
-// adds into another's output: no atomics, deterministic results.  Causal work
-// skips the tiles above the diagonal and masks only those that cross it or
-// the end of the sequence.
+// pass does 7 tile products instead of 5 (the dQ pass forms S and dP again),
+// and in exchange no workgroup ever adds into another's output: no atomics,
+// deterministic results.  Causal work skips the tiles above the diagonal and
+// masks only those that cross it or the end of the sequence.
 //
 // Register layouts of the 32x32x16 bf16 instruction: attn_bf16_common.h.
 #include "attn_bf16_common.h"
@@ -124,40 +121,48 @@ __device__ __forceinline__ int tchunk(int d, int c) {
 }
 
 // ---------------------------------------------------------------------------
-// dV and dK passes
-constexpr int KV_NT = 512;   // 8 waves, two per SIMD
+// dK and dV in one pass.  One workgroup = 4 waves, one per SIMD, owns 128 keys,
+// 32 per wave, with K and V of its keys in registers as the B operands of S and
+// dP.  At one wave per SIMD a wave may use 512 registers, and the compiler
+// keeps the matrix accumulators (dK, dV, S, dP: 160 per lane) in AGPRs; at two
+// waves per SIMD they would not fit.  32-query tiles of Q, dO, their d-major
+// copies, LSE and Delta stream through LDS by DMA, double buffered, from the
+// end of the sequence down: every workgroup of a head reads the same tile at
+// about the same time, so the head's query-side data passes through the XCD's
+// L2 once.  Per tile: S = Q K^T and dP = dO V^T (A operands: Q and dO rows,
+// permuted), P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS (A
+// operands from the d-major tiles).
+constexpr int KV_NT = 256;   // 4 waves, one per SIMD
 constexpr int KV_KW = 32;    // keys per wave
-constexpr int KV_BK = 256;   // keys per workgroup
+constexpr int KV_BK = 128;   // keys per workgroup
 constexpr int KV_TQ = 32;    // queries per tile
 
-// GK = false: G = dV; GK = true: G = dK (scaled by gscale = scale).
-template <int D, bool CAUSAL, bool GK>
-__global__ __launch_bounds__(KV_NT, 1) void attn_bwd_kv_kernel(
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT,
-    const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ G, int N, int nkb, int nb,
-    int total, float c, float gscale) {
+    const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    int N, int nkb, int nb, int total, float c, float scale) {
   constexpr int CPR = D / 8;
   constexpr int NW = KV_NT / 64;
-  constexpr int ROW_CHUNKS = KV_TQ * CPR;          // a row-major tile of 32 tokens
-  constexpr int T_CHUNKS = D * (KV_TQ / 8);        // a d-major tile of 32 tokens
-  static_assert(ROW_CHUNKS <= 64 * NW && T_CHUNKS <= 64 * NW, "one DMA instruction per wave and tile");
-  __shared__ uint4 qbuf0[ROW_CHUNKS], qbuf1[ROW_CHUNKS];                       // Q rows
-  __shared__ uint4 obuf0[GK ? ROW_CHUNKS : 1], obuf1[GK ? ROW_CHUNKS : 1];     // dO rows (dK pass)
-  __shared__ uint4 tbuf0[T_CHUNKS], tbuf1[T_CHUNKS];                           // dO^T (dV) or Q^T (dK)
+  constexpr int ROW_CHUNKS = KV_TQ * CPR;
+  constexpr int T_CHUNKS = D * (KV_TQ / 8);
+  constexpr int RPW = (ROW_CHUNKS + KV_NT - 1) / KV_NT;   // DMA instructions per wave and row tile
+  constexpr int TPW = (T_CHUNKS + KV_NT - 1) / KV_NT;
+  __shared__ uint4 qbuf0[ROW_CHUNKS], qbuf1[ROW_CHUNKS], obuf0[ROW_CHUNKS], obuf1[ROW_CHUNKS];
+  __shared__ uint4 qtb0[T_CHUNKS], qtb1[T_CHUNKS], otb0[T_CHUNKS], otb1[T_CHUNKS];
   __shared__ float lbuf0[KV_TQ], lbuf1[KV_TQ], dbuf0[KV_TQ], dbuf1[KV_TQ];
 
   const int L = xcd_logical_id(blockIdx.x, total);
   const int bh = L / nkb;
-  const int k0 = (L - bh * nkb) * KV_BK;     // causal: low key blocks (the most work) first
+  const int k0 = (L - bh * nkb) * KV_BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int kw0 = k0 + KV_KW * wave;
-  const int key = kw0 + l32;                 // this lane's key
+  const int key = kw0 + l32;
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t nbytes = (uint32_t)N * D * 2;
 
-  // K (and V for dK) of this lane's key as B operands: dims 16 dc + 8 half + 0..7
   bf16x8 kf[D / 16], vf[D / 16];
   {
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + hoff), 0, nbytes, 0x00020000);
@@ -166,13 +171,9 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_kv_kernel(
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
       kf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32 * dc, 0, 0));
-      if (GK) vf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 32 * dc, 0, 0));
+      vf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 32 * dc, 0, 0));
     }
   }
-
-  // LDS byte offsets of this lane's reads: rows of the row-major tiles (A
-  // operand of S and dP, rows permuted) and chunks of the d-major tile (A
-  // operand of the dV / dK products: row 32 db + l32, chunk 2 qc + half)
   uint32_t koff[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) koff[dc] = 16 * lds_chunk<D>(key_of_arow(l32), 2 * dc + half);
@@ -180,77 +181,80 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_kv_kernel(
 #pragma unroll
   for (int qc = 0; qc < 2; ++qc) toff[qc] = 16 * tchunk<KV_TQ>(l32, 2 * qc + half);
 
-  // DMA: each wave fills 64 consecutive slots of each tile (waves past the
-  // tile's size skip); rows past the end of the sequence read as zeros, which
-  // makes their terms vanish (dO = 0, and Q = 0 with Delta = 0 gives dS = 0)
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + hoff), 0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + hoff), 0, nbytes, 0x00020000);
   const size_t thoff = (size_t)bh * nb * D * TT;
-  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((GK ? QT : dOT) + thoff), 0, (uint32_t)nb * D * TT * 2, 0x00020000);
+  const uint32_t tbytes = (uint32_t)nb * D * TT * 2;
+  const __amdgpu_buffer_rsrc_t qtrs = __builtin_amdgcn_make_buffer_rsrc((void*)(QT + thoff), 0, tbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t otrs = __builtin_amdgcn_make_buffer_rsrc((void*)(dOT + thoff), 0, tbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + (size_t)bh * N), 0, (uint32_t)N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t drs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(Dl + (size_t)bh * N), 0, (uint32_t)N * 4, 0x00020000);
-  const int slot = wave * 64 + lane;
-  uint32_t row_off, t_off;
-  {
-    const int r = slot / CPR, ch = slot % CPR;
-    row_off = (uint32_t)(r * D + 8 * (ch ^ swz<D>(r))) * 2;
-    const int d = slot / (KV_TQ / 8), cc = slot % (KV_TQ / 8);
-    t_off = (uint32_t)(d * TT * 2 + 16 * (cc ^ ((d >> 2) & 3)));
+  uint32_t row_off[RPW], t_off[TPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane, r = slot / CPR, ch = slot % CPR;
+    row_off[i] = (uint32_t)(r * D + 8 * (ch ^ swz<D>(r))) * 2;
   }
-  auto issue_tile = [&](int q0, uint4* qd, uint4* od, uint4* td, float* ld, float* dd) {
-    if (wave * 64 < ROW_CHUNKS) {
-      lds_dma16(qrs, qd + wave * 64, row_off, (uint32_t)q0 * D * 2);
-      if (GK) lds_dma16(ors, od + wave * 64, row_off, (uint32_t)q0 * D * 2);
-    }
-    if (wave * 64 < T_CHUNKS) lds_dma16(trs, td + wave * 64, t_off, (uint32_t)((q0 / TT) * D * TT + q0 % TT) * 2);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane, d = slot / (KV_TQ / 8), cc = slot % (KV_TQ / 8);
+    t_off[i] = (uint32_t)(d * TT * 2 + 16 * (cc ^ ((d >> 2) & 3)));
+  }
+  auto issue_tile = [&](int q0, uint4* qd, uint4* od, uint4* qtd, uint4* otd, float* ld, float* dd) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if ((i * NW + wave) * 64 < ROW_CHUNKS) {
+        lds_dma16(qrs, qd + (i * NW + wave) * 64, row_off[i], (uint32_t)q0 * D * 2);
+        lds_dma16(ors, od + (i * NW + wave) * 64, row_off[i], (uint32_t)q0 * D * 2);
+      }
+    const uint32_t tb = (uint32_t)((q0 / TT) * D * TT + q0 % TT) * 2;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      if ((i * NW + wave) * 64 < T_CHUNKS) {
+        lds_dma16(qtrs, qtd + (i * NW + wave) * 64, t_off[i], tb);
+        lds_dma16(otrs, otd + (i * NW + wave) * 64, t_off[i], tb);
+      }
     if (wave == 0 && lane < KV_TQ / 4) {
       lds_dma16(lrs, ld, 16 * lane, (uint32_t)q0 * 4);
-      if (GK) lds_dma16(drs, dd, 16 * lane, (uint32_t)q0 * 4);
+      lds_dma16(drs, dd, 16 * lane, (uint32_t)q0 * 4);
     }
   };
 
-  f32x16 acc[D / 32];
+  f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      dka[db][r] = 0.0f;
+      dva[db][r] = 0.0f;
+    }
 
-  // one tile: register r of half h is query q0 + 16 (r / 8) + 8 h + r % 8
-  auto tile = [&](auto maskc, const char* qt, const char* ot, const char* tt, const float* l2t, const float* dlt,
-                  int q0) {
+  auto tile = [&](auto maskc, const char* qt, const char* ot, const char* qtt, const char* ott, const float* l2t,
+                  const float* dlt, int q0) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
-    f32x16 s;
+    f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.0f;
+      dp[r] = 0.0f;
+    }
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + koff[dc]), kf[dc], s, 0,
-                                                 0, 0);
-    f32x16 dp;
-    if (GK) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ot + koff[dc]), vf[dc], dp,
-                                                    0, 0, 0);
+    for (int dc = 0; dc < D / 16; ++dc) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + koff[dc]), kf[dc], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ot + koff[dc]), vf[dc], dp, 0,
+                                                  0, 0);
     }
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       const float4 la = *reinterpret_cast<const float4*>(l2t + 16 * qc + 8 * half);
       const float4 lb = *reinterpret_cast<const float4*>(l2t + 16 * qc + 8 * half + 4);
+      const float4 da = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half);
+      const float4 dbv = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half + 4);
       const float l2v[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-      float dlv[8];
-      if (GK) {
-        const float4 da = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half);
-        const float4 dbv = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half + 4);
-        dlv[0] = da.x; dlv[1] = da.y; dlv[2] = da.z; dlv[3] = da.w;
-        dlv[4] = dbv.x; dlv[5] = dbv.y; dlv[6] = dbv.z; dlv[7] = dbv.w;
-      }
-      bf16x8 b;
+      const float dlv[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
+      bf16x8 pb, dsb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * qc + e], c, -l2v[e]));
@@ -258,58 +262,60 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_kv_kernel(
           const int q = q0 + 16 * qc + 8 * half + e;
           if (key >= N || (CAUSAL && key > q)) p = 0.0f;
         }
-        b[e] = GK ? (__bf16)(p * (dp[8 * qc + e] - dlv[e])) : (__bf16)p;
+        pb[e] = (__bf16)p;
+        dsb[e] = (__bf16)(p * (dp[8 * qc + e] - dlv[e]));
       }
-      // dV^T += dO^T P  or  dK^T += Q^T dS: A operand from the d-major tile
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(tt + toff[qc] + db * 32 * KV_TQ * 2), b, acc[db], 0, 0, 0);
+      for (int db = 0; db < D / 32; ++db) {
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(ott + toff[qc] + db * 32 * KV_TQ * 2), pb, dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(qtt + toff[qc] + db * 32 * KV_TQ * 2), dsb, dka[db], 0, 0, 0);
+      }
     }
   };
 
-  // Query tiles are walked from the end of the sequence down, so that every
-  // workgroup of a head (each starting at its own first key when causal) reads
-  // the same tile at about the same time and the head's query-side data is
-  // fetched from HBM once, through the XCD's L2.
-  const int qstart = CAUSAL ? k0 : 0;        // queries before the first key see none of these keys
+  const int qstart = CAUSAL ? k0 : 0;
   const int ntiles = (N - qstart + KV_TQ - 1) / KV_TQ;
-  const int qtop = qstart + (ntiles - 1) * KV_TQ;   // first query of the first tile walked
+  const int qtop = qstart + (ntiles - 1) * KV_TQ;
   const bool active = kw0 < N;
   const bool ktail = kw0 + KV_KW > N;
-
-  auto step = [&](int t, const uint4* qc, const uint4* oc, const uint4* tc, const float* lc, const float* dlc,
-                  uint4* qn, uint4* on, uint4* tn, float* ln, float* dn) {
+  auto step = [&](int t, const uint4* qc, const uint4* oc, const uint4* qtc, const uint4* otc, const float* lc,
+                  const float* dlc, uint4* qn, uint4* on, uint4* qtn, uint4* otn, float* ln, float* dn)
+      __attribute__((always_inline)) {
     const int q0 = qtop - t * KV_TQ;
-    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's part of tile t has landed
-    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's reads of the other buffers are done
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __asm__ volatile("s_barrier" ::: "memory");
-    if (t + 1 < ntiles) issue_tile(q0 - KV_TQ, qn, on, tn, ln, dn);
-    if (!active || (CAUSAL && q0 + KV_TQ - 1 < kw0)) return;   // no query of the tile sees these keys
+    if (t + 1 < ntiles) issue_tile(q0 - KV_TQ, qn, on, qtn, otn, ln, dn);
+    if (!active || (CAUSAL && q0 + KV_TQ - 1 < kw0)) return;
     const char* qt = reinterpret_cast<const char*>(qc);
     const char* ot = reinterpret_cast<const char*>(oc);
-    const char* tt = reinterpret_cast<const char*>(tc);
-    if (ktail || (CAUSAL && q0 < kw0 + KV_KW - 1)) tile(IC<1>{}, qt, ot, tt, lc, dlc, q0);
-    else tile(IC<0>{}, qt, ot, tt, lc, dlc, q0);
+    const char* qtt = reinterpret_cast<const char*>(qtc);
+    const char* ott = reinterpret_cast<const char*>(otc);
+    if (ktail || (CAUSAL && q0 < kw0 + KV_KW - 1)) tile(IC<1>{}, qt, ot, qtt, ott, lc, dlc, q0);
+    else tile(IC<0>{}, qt, ot, qtt, ott, lc, dlc, q0);
   };
-
-  issue_tile(qtop, qbuf0, obuf0, tbuf0, lbuf0, dbuf0);
+  issue_tile(qtop, qbuf0, obuf0, qtb0, otb0, lbuf0, dbuf0);
   for (int t = 0; t < ntiles; t += 2) {
-    step(t, qbuf0, obuf0, tbuf0, lbuf0, dbuf0, qbuf1, obuf1, tbuf1, lbuf1, dbuf1);
-    if (t + 1 < ntiles) step(t + 1, qbuf1, obuf1, tbuf1, lbuf1, dbuf1, qbuf0, obuf0, tbuf0, lbuf0, dbuf0);
+    step(t, qbuf0, obuf0, qtb0, otb0, lbuf0, dbuf0, qbuf1, obuf1, qtb1, otb1, lbuf1, dbuf1);
+    if (t + 1 < ntiles)
+      step(t + 1, qbuf1, obuf1, qtb1, otb1, lbuf1, dbuf1, qbuf0, obuf0, qtb0, otb0, lbuf0, dbuf0);
   }
-
-  // G = gscale acc^T; register 4 a + i of block db is dim 32 db + 8 a + 4 half + i
   if (key < N) {
-    uint16_t* grow = G + hoff + (size_t)key * D;
+    uint16_t* krow = dK + hoff + (size_t)key * D;
+    uint16_t* vrow = dV + hoff + (size_t)key * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = 32 * db + 8 * a + 4 * half;
-        const bf16x4_t w = {(__bf16)(acc[db][4 * a + 0] * gscale), (__bf16)(acc[db][4 * a + 1] * gscale),
-                            (__bf16)(acc[db][4 * a + 2] * gscale), (__bf16)(acc[db][4 * a + 3] * gscale)};
-        *reinterpret_cast<bf16x4_t*>(grow + d0) = w;
+        const bf16x4_t wk = {(__bf16)(dka[db][4 * a + 0] * scale), (__bf16)(dka[db][4 * a + 1] * scale),
+                             (__bf16)(dka[db][4 * a + 2] * scale), (__bf16)(dka[db][4 * a + 3] * scale)};
+        const bf16x4_t wv = {(__bf16)dva[db][4 * a + 0], (__bf16)dva[db][4 * a + 1], (__bf16)dva[db][4 * a + 2],
+                             (__bf16)dva[db][4 * a + 3]};
+        *reinterpret_cast<bf16x4_t*>(krow + d0) = wk;
+        *reinterpret_cast<bf16x4_t*>(vrow + d0) = wv;
       }
   }
 }
@@ -530,12 +536,8 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   const float c = (float)((double)scale * 1.4426950408889634);
   const int nkb = (N + KV_BK - 1) / KV_BK;
   const int tkv = nkb * B * H;
-  hipLaunchKernelGGL((attn_bwd_kv_kernel<D, CAUSAL, false>), dim3(tkv), dim3(KV_NT), 0, stream, Q, K, V, dO, w.qt,
-                     w.ot, w.l2, w.dl, static_cast<uint16_t*>(dv), N, nkb, nb, tkv, c, 1.0f);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_kv_kernel<D, CAUSAL, true>), dim3(tkv), dim3(KV_NT), 0, stream, Q, K, V, dO, w.qt,
-                     w.ot, w.l2, w.dl, static_cast<uint16_t*>(dk), N, nkb, nb, tkv, c, scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3(tkv), dim3(KV_NT), 0, stream, Q, K, V, dO, w.qt, w.ot,
+                     w.l2, w.dl, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, nkb, nb, tkv, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (N + DQ_BR - 1) / DQ_BR;
