@@ -116,3 +116,35 @@ def test_bwd_workload_sampled_heads(gpu):
     # launch configuration the benchmark times; two heads checked in full
     w = WORKLOADS["bf16_causal_8k_bwd"]
     _check(w.B, w.H, w.N, w.d, w.causal, seed=w.seed, heads=[(0, 0), (1, 15)])
+
+
+def test_bwd_identities_at_32k(gpu):
+    # the 32k-token layer (1 x 32 heads x 32768 tokens, causal): too large for the
+    # oracle, so the identities of the gradients are checked on every head, in
+    # float64 from the GPU's bf16 results: sum_j dV_j = sum_i dO_i (rows of P sum
+    # to one), sum_j dK_j = 0 (rows of dS sum to zero), <Q, dQ> = <K, dK> (S is
+    # bilinear).  Bounds: the bf16 rounding of each gradient element (2^-9
+    # relative) averages out over 32768 rows; 1e-2 of each side's magnitude
+    # leaves room for the float32 arithmetic.  <Q, dQ> = sum_ij dS_ij S_ij is a
+    # sum whose terms nearly cancel (each row of dS sums to zero), so its bound
+    # is taken against the size of the terms, sum |Q * dQ| + sum |K * dK|.
+    w = WORKLOADS["bf16_causal_32k"].with_shape(backward=True)
+    q, k, v = make_qkv(w)
+    do = make_dout(w)
+    log(f"[bwd identities] B={w.B} H={w.H} N={w.N} d={w.d} causal")
+    dq, dk, dv = _gpu_grads(q, k, v, do, w.causal, w.scale)
+    qd, kd, dod = (t.to("cuda:0").double() for t in (q, k, do))
+    dq, dk, dv = dq.double(), dk.double(), dv.double()
+    sdv, sdo = dv.sum(dim=2), dod.sum(dim=2)                     # [B, H, d]
+    e1 = float(((sdv - sdo).norm(dim=-1) / sdo.norm(dim=-1)).max())
+    sdk = dk.sum(dim=2).norm(dim=-1)
+    e2 = float((sdk / dk.abs().sum(dim=2).norm(dim=-1)).max())
+    a, b = (qd * dq).sum(dim=(2, 3)), (kd * dk).sum(dim=(2, 3))
+    mag = (qd * dq).abs().sum(dim=(2, 3)) + (kd * dk).abs().sum(dim=(2, 3))
+    e3 = float(((a - b).abs() / mag).max())
+    kappa = float((mag / (a.abs() + b.abs())).max())
+    log(f"  sum dV vs sum dO {e1:.3g}, |sum dK| / sum|dK| {e2:.3g}, <Q,dQ> vs <K,dK> {e3:.3g} of the terms' size "
+        f"(cancellation factor up to {kappa:.3g})")
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    assert e1 <= 1e-2 and e2 <= 1e-2 and e3 <= 1e-3
