@@ -105,6 +105,45 @@ __device__ __forceinline__ void pv_tile(const char* vt, const uint32_t (&voff)[D
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
+// Both products of a matrix half, O^T += V_(j-1)^T P_(j-1)^T and
+// S_j^T = K_j Q^T, with their matrix ops alternating.  The P V operands come
+// through the slower transposed LDS reads and the S operands through 16-byte
+// reads; alternating the two streams spreads the LDS traffic evenly over the
+// matrix work instead of running the LDS-heavy half first, and the matrix core
+// never drains between the two products.
+__device__ __forceinline__ void pv_score_tile(const char* vt, const char* kt, const uint32_t (&voff)[D / 32][2],
+                                              const uint32_t (&koff)[D / 16], const bf16x8 (&pb)[BC / 16],
+                                              const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
+                                              f32x16 (&s)[BC / 32]) {
+  constexpr int KB_BYTES = 32 * D * 2;   // one 32-key block of the K tile
+  constexpr int KC_BYTES = 16 * D * 2;   // one 16-key chunk of the V tile
+  constexpr int NSTEP = (D / 32) * (BC / 16);
+  static_assert(NSTEP == (D / 16) * (BC / 32), "both products have the same number of matrix ops");
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    const int kc = i / (D / 32), db = i % (D / 32);
+    const bf16x4_t v0 = tr_read(vt + voff[db][0] + kc * KC_BYTES);
+    const bf16x4_t v1 = tr_read(vt + voff[db][1] + kc * KC_BYTES);
+    const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], acc[db], 0, 0, 0);
+    const int dc = i / (BC / 32), kb = i % (BC / 32);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[dc] + kb * KB_BYTES);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
+  }
+  // three steps of reads (2 transposed + 1 plain each) in flight ahead of the matrix ops
+  __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+#pragma unroll
+  for (int i = 0; i < NSTEP - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+}
+
 // Online softmax of one tile: mask (MASK: the tile crosses this wave's
 // diagonal or the end of the sequence), running maximum with lazy rescaling of
 // O, p = exp2(c s - m2) rounded to bf16 as the B operand of P V, and the
@@ -164,9 +203,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int BH, int groups, float c,
     uint32_t qflip) {
   // Separate objects, so that the compiler never orders a read of one buffer
-  // after a DMA into the other.
-  __shared__ uint4 kbuf0[TILE_CHUNKS], kbuf1[TILE_CHUNKS];
-  __shared__ uint4 vbuf0[TILE_CHUNKS], vbuf1[TILE_CHUNKS];
+  // after a DMA into the other.  The larger alignment places the four tile
+  // buffers ahead of the Q rows, in the first 64 KB of LDS, where every tile
+  // read addresses its buffer through the 16-bit immediate offset instead of
+  // a per-read address add.
+  __shared__ __attribute__((aligned(256))) uint4 kbuf0[TILE_CHUNKS], kbuf1[TILE_CHUNKS];
+  __shared__ __attribute__((aligned(256))) uint4 vbuf0[TILE_CHUNKS], vbuf1[TILE_CHUNKS];
   __shared__ uint4 qsm[BR * CPR];            // the item's Q rows (swizzled), each wave's own 32 rows
 
   // Static work list: workgroup g serves heads [xg * hx, (xg + 1) * hx) with
@@ -319,8 +361,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
         if (j < ntiles) issue_tile(V, vcur, bh, j * BC);
       }
       if ((grp == 0) == !odd) {              // matrix half
-        if (j >= 1 && active(j - 1)) pv_tile(reinterpret_cast<const char*>(vprev), voff, pb, acc);
-        if (active(j)) score_tile(reinterpret_cast<const char*>(kcur), koff, qf, s);
+        const bool do_pv = j >= 1 && active(j - 1), do_s = active(j);
+        if (do_pv && do_s) {
+          pv_score_tile(reinterpret_cast<const char*>(vprev), reinterpret_cast<const char*>(kcur), voff, koff, pb, qf,
+                        acc, s);
+        } else {
+          if (do_pv) pv_tile(reinterpret_cast<const char*>(vprev), voff, pb, acc);
+          if (do_s) score_tile(reinterpret_cast<const char*>(kcur), koff, qf, s);
+        }
         if (j == nt2) epilogue();
       } else {                               // softmax half: tile j (group 0) or j - 1 (group 1)
         const int js = odd ? j : j - 1;
