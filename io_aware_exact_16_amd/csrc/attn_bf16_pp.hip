@@ -144,11 +144,40 @@ __device__ __forceinline__ void pv_score_tile(const char* vt, const char* kt, co
   __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
 }
 
+// p = exp2(c s - m2) for this lane's 32 scores of one tile, rounded to bf16
+// as the B operand of P V; returns the lane's float32 sum of p (summing the
+// bf16-rounded p would cost up to 2^-9 relative in l, i.e. in LSE, on rows
+// with few keys).  Masked keys give exact zeros, also when c = 0.
+template <bool MASK>
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16], float m2, float c) {
+  float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float s0 = s[kc >> 1][8 * (kc & 1) + e], s1 = s[kc >> 1][8 * (kc & 1) + e + 1];
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m2));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m2));
+      if (MASK) {
+        p0 = s0 == -INFINITY ? 0.0f : p0;
+        p1 = s1 == -INFINITY ? 0.0f : p1;
+      }
+      rs[e >> 1] += p0 + p1;
+      pb[kc][e] = (__bf16)p0;
+      pb[kc][e + 1] = (__bf16)p1;
+    }
+  return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+}
+
 // Online softmax of one tile: mask (MASK: the tile crosses this wave's
-// diagonal or the end of the sequence), running maximum with lazy rescaling of
-// O, p = exp2(c s - m2) rounded to bf16 as the B operand of P V, and the
-// float32 row sum (summing the bf16-rounded p would cost up to 2^-9 relative in
-// l, i.e. in LSE, on rows with few keys).
+// diagonal or the end of the sequence), p against the running reference
+// maximum m2, and the row sum.  The reference only has to keep every p
+// finite and in range, so the tile maximum is not formed on the common path:
+// p is computed against the current m2 first, and only if a lane's sum of its
+// 32 p exceeds 2^8 (some p may be above 2^8), or is not finite (the first
+// tile, where m2 = -inf), does the wave form the tile maximum, move m2 to it,
+// rescale O and l, and compute p again.  A lane sum of at most 2^8 bounds each
+// of its p by 2^8, which is exact in float32 and in bf16 range.
 template <bool MASK>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16], f32x16 (&acc)[D / 32],
                                              float& m2, float& lsum, float c, int j0, int qi, int N, int half) {
@@ -161,41 +190,28 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[BC / 32], bf16x8 (&pb)[
         if (key >= N || key > qi) s[kb][r] = -INFINITY;
       }
   }
-  float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // 4 independent chains
+  float part = exp_tile<MASK>(s, pb, m2, c);
+  if (__any(!(part <= 256.0f))) {
+    float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // 4 independent chains
 #pragma unroll
-  for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pm[(kb * 2 + (r >> 3)) & 3] = fmaxf(pm[(kb * 2 + (r >> 3)) & 3], s[kb][r]);
-  float tmax = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
-  tmax = wave_halves_max(tmax);
-  const float tm2 = tmax * c;
-  if (__any(tm2 > m2 + RESCALE_THRESHOLD)) {
-    const float mnew = fmaxf(m2, tm2);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      for (int r = 0; r < 16; ++r) pm[(kb * 2 + (r >> 3)) & 3] = fmaxf(pm[(kb * 2 + (r >> 3)) & 3], s[kb][r]);
+    float tmax = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+    tmax = wave_halves_max(tmax);
+    const float tm2 = tmax * c;
+    if (tm2 > m2) {
+      const float alpha = __builtin_amdgcn_exp2f(m2 - tm2);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    lsum *= alpha;
-    m2 = mnew;
-  }
-  float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int kc = 0; kc < BC / 16; ++kc)
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float s0 = s[kc >> 1][8 * (kc & 1) + e], s1 = s[kc >> 1][8 * (kc & 1) + e + 1];
-      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -m2));
-      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -m2));
-      if (MASK) {                        // exact zeros for masked keys, also when c = 0
-        p0 = s0 == -INFINITY ? 0.0f : p0;
-        p1 = s1 == -INFINITY ? 0.0f : p1;
-      }
-      rs[e >> 1] += p0 + p1;
-      pb[kc][e] = (__bf16)p0;
-      pb[kc][e + 1] = (__bf16)p1;
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m2 = tm2;
     }
-  lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    part = exp_tile<MASK>(s, pb, m2, c);
+  }
+  lsum += part;
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
