@@ -23,7 +23,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 constexpr int BC = 64;    // key rows per tile
-constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the allowed growth of p
 
 // Position (in 16-byte chunks) of chunk `ch` of tile row `row` in LDS.  The
 // XOR swizzle makes both read patterns of the kernel conflict-free: 16 lanes
@@ -122,32 +121,12 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
       }
   }
 
-  float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // 4 independent chains
-#pragma unroll
-  for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pm[(kb * 2 + (r >> 3)) & 3] = fmaxf(pm[(kb * 2 + (r >> 3)) & 3], s[kb][r]);
-  float tmax = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
-  tmax = wave_halves_max(tmax);
-  const float tm2 = tmax * c;
-  if (__any(tm2 > m2 + RESCALE_THRESHOLD)) {
-    const float mnew = fmaxf(m2, tm2);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    lsum *= alpha;
-    m2 = mnew;
-  }
-
   // p = exp2(c s - m2), rounded to bf16 as the B operand of P V; the row sum
   // uses the float32 p (summing the bf16-rounded values would cost up to 2^-9
-  // relative in l, i.e. in LSE, on rows with few keys).  P of chunk kc+1 is
-  // computed while the matrix ops of chunk kc run.
+  // relative in l, i.e. in LSE, on rows with few keys).
   bf16x8 pb[BC / 16];
-  float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto pchunk = [&](int kc) {
+  auto pchunk = [&](int kc) -> float {
+    float r[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const float s0 = s[kc >> 1][8 * (kc & 1) + e], s1 = s[kc >> 1][8 * (kc & 1) + e + 1];
@@ -157,14 +136,42 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
         p0 = s0 == -INFINITY ? 0.0f : p0;
         p1 = s1 == -INFINITY ? 0.0f : p1;
       }
-      rs[e >> 1] += p0 + p1;
+      r[(e >> 1) & 1] += p0 + p1;
       pb[kc][e] = (__bf16)p0;
       pb[kc][e + 1] = (__bf16)p1;
     }
+    return r[0] + r[1];
   };
-  pchunk(0);
+  // The reference maximum m2 only has to keep every p finite and in range, so
+  // the tile maximum is not formed on the common path.  A tile whose lane sum
+  // of p is at most 2^8 has every p at most 2^8; a larger or non-finite sum
+  // (the first tile, where m2 = -inf) moves m2 to the tile maximum, rescales O
+  // and l, and computes P again.
+  auto move_reference = [&]() {
+    float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // 4 independent chains
 #pragma unroll
-  for (int kc = 0; kc < BC / 16; ++kc) {
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pm[(kb * 2 + (r >> 3)) & 3] = fmaxf(pm[(kb * 2 + (r >> 3)) & 3], s[kb][r]);
+    const float tm2 = wave_halves_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]))) * c;
+    if (tm2 > m2) {
+      const float alpha = __builtin_amdgcn_exp2f(m2 - tm2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m2 = tm2;
+    }
+  };
+  // all four chunks of P first, one range check for the tile, then P V
+  float cs = (pchunk(0) + pchunk(1)) + (pchunk(2) + pchunk(3));
+  if (__any(!(cs <= 256.0f))) {
+    move_reference();
+    cs = (pchunk(0) + pchunk(1)) + (pchunk(2) + pchunk(3));
+  }
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const bf16x4_t v0 = tr_read(vt + voff[db][0] + kc * KC_BYTES);
@@ -172,23 +179,16 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
       const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], acc[db], 0, 0, 0);
     }
-    if (kc + 1 < BC / 16) pchunk(kc + 1);
-  }
-  lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-  // schedule: P chunk 0, then per chunk: its 8 transposed V reads, and its 4
-  // matrix ops each followed by a quarter of the next chunk's VALU work
-  constexpr int VPC = MASK ? 28 : 20;      // VALU instructions per P chunk
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 1);
-  __builtin_amdgcn_sched_group_barrier(0x002, VPC, 1);
+  // keep 8 transposed reads (4 matrix ops' operands) in flight
+  constexpr int NPV = (D / 32) * (BC / 16);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-  for (int kc = 0; kc < BC / 16; ++kc) {
-    if (kc + 1 < BC / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 1);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (kc + 1 < BC / 16) __builtin_amdgcn_sched_group_barrier(0x002, VPC / (D / 32), 1);
-    }
+  for (int i = 0; i < NPV - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  lsum += cs;
 }
 
 }  // namespace bf16k
