@@ -150,6 +150,34 @@ def test_unusual_scales(gpu, scale):
         compare(o, lse, o_ref, lse_ref, "bf16")
 
 
+def _jumping_keys(N, d, seed, gain):
+    """Q, K, V ~ N(0,1) with the keys scaled up in steps along the sequence
+    (x1 up to key 299, x4 up to 699, x gain after), so that the row maxima of
+    the scaled scores jump between key tiles instead of settling early."""
+    q, k, v = make_qkv(custom(1, 2, N, d, False, "bf16", seed=seed))
+    g = torch.ones(N)
+    g[300:700] = 4.0
+    g[700:] = gain
+    k = (k.float() * g[None, None, :, None]).to(torch.bfloat16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("gain", [16.0, 40.0])
+def test_scores_jump_between_tiles(gpu, d, causal, gain):
+    # The softmax keeps a reference maximum that it moves only when a tile's
+    # p would leave its range.  Keys that grow along the sequence move it in
+    # the middle of rows; with gain 40 the later scores exceed the early
+    # reference by more than 2^128 in the exp2 domain, so p computed against
+    # the old reference would overflow before the reference moves.
+    q, k, v = _jumping_keys(1500, d, 21 + d, gain)
+    scale = d ** -0.5
+    o, lse = run_attention(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), scale, causal)
+    compare(o, lse, o_ref, lse_ref, "bf16")
+
+
 def test_incoherent_inputs_match_oracle(gpu):
     # Q H and K H (normalised Hadamard) as inputs: same parity bar
     q, k, v = make_qkv(custom(1, 2, 1000, 128, True, "bf16", seed=10, outlier_frac=0.001))

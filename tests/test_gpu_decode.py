@@ -53,6 +53,26 @@ def test_decode_long_keys(gpu):
     _decode_check(1, 4, 1, 32768, 128, True, seed=77)
 
 
+def test_decode_scores_jump_between_tiles(gpu):
+    # keys scaled up in steps along the sequence: the reference maximum of each
+    # split-KV chunk moves mid-chunk, and by more than 2^128 (exp2 domain) at
+    # the last step
+    w = custom(1, 2, 3000, 128, True, "bf16", seed=83, n_q=4)
+    q, k, v = make_qkv(w)
+    g = torch.ones(3000)
+    g[900:1800] = 4.0
+    g[1800:] = 40.0
+    k = (k.float() * g[None, None, :, None]).to(torch.bfloat16)
+    o, lse = fa.attention_decode(*to_dev(q, k, v), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = f64(o), f64(lse)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), w.scale, True, q_index=oracle.decode_positions(4, 3000))
+    tol_o, tol_l = TOL["bf16"]
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert float(np.abs(o - ro).max()) <= tol_o
+    assert float((np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))).max()) <= tol_l
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125])
 def test_decode_unusual_scales(gpu, scale):
     _decode_check(1, 2, 3, 2000, 128, True, seed=78, scale=scale)
