@@ -131,13 +131,17 @@ __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const void* _
             x[i + s] = a - b;
           }
       if (TPR == 2) {   // stride-64 stage: partner element sits in the adjacent lane
+        // part 0 keeps x + other, part 1 other - x: one FMA with a +-1 factor
+        // (exact like the add), and a lane swap that every lane sources, so
+        // the DPP move needs no fallback value
+        const T sgn = part == 0 ? (T)1 : (T)-1;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
           const uint64_t bits = __double_as_longlong((double)x[i]);
-          const uint32_t lo = __builtin_amdgcn_update_dpp(0, (uint32_t)bits, 0xB1, 0xF, 0xF, false);
-          const uint32_t hi = __builtin_amdgcn_update_dpp(0, (uint32_t)(bits >> 32), 0xB1, 0xF, 0xF, false);
+          const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)bits, 0xB1, 0xF, 0xF, false);
+          const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(bits >> 32), 0xB1, 0xF, 0xF, false);
           const T other = (T)__longlong_as_double(((uint64_t)hi << 32) | lo);
-          x[i] = part == 0 ? x[i] + other : other - x[i];
+          x[i] = __builtin_fma(x[i], sgn, other);
         }
       }
     }
