@@ -21,10 +21,13 @@
 //    belong to the same workgroup, so neither finishes early.
 //  * 8 waves = 2 groups of 4; waves w and w + 4 share a SIMD (measured), each
 //    wave owns 32 query rows, and the 8 waves share every K/V tile in LDS.
-//  * phases separated by s_barrier: in even phase 2j group 0 runs the matrix
-//    half M(j) = { O^T += V_(j-1)^T P_(j-1)^T ; S_j^T = K_j Q^T } while group 1
+//  * phases: in even phase 2j group 0 runs the matrix half
+//    M(j) = { O^T += V_(j-1)^T P_(j-1)^T ; S_j^T = K_j Q^T } while group 1
 //    runs the softmax of tile j-1; in odd phase 2j+1 the roles swap.  So each
-//    SIMD always has one wave on the matrix cores and one on the VALU.
+//    SIMD has one wave on the matrix cores and one on the VALU.  An s_barrier
+//    opens every even phase; the swap into the odd phase is not synchronised
+//    (a wave goes on as soon as its own half is done), since no LDS buffer
+//    changes hands there: the odd barrier only held early waves back.
 //  * tiles of 64 keys are DMA'd HBM/L2 -> LDS (buffer_load ... lds, no
 //    staging registers) into two K and two V buffers: K_j in phase 2j - 2,
 //    V_j in phase 2j, each two phases before its first use; every even phase
@@ -362,8 +365,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
       constexpr int JP = decltype(jpc)::value;
       const int j = p >> 1;
       const bool odd = p & 1;
-      if (!odd && p != 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the DMAs of phase p - 2 landed
-      __asm__ volatile("s_barrier" ::: "memory");
+      if (!odd) {
+        if (p != 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the DMAs of phase p - 2 landed
+        __asm__ volatile("s_barrier" ::: "memory");
+      }
       uint4* const kcur = JP ? kbuf1 : kbuf0;   // K_j
       uint4* const knext = JP ? kbuf0 : kbuf1;  // K_(j+1)
       uint4* const vcur = JP ? vbuf1 : vbuf0;   // V_j (loaded now, read in phases 2j + 2, 2j + 3)
