@@ -175,7 +175,12 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_fp8_kernel(
+// Three waves per SIMD for causal attention: this kernel is bound by its
+// softmax VALU work, and a third resident wave fills more of the VALU's idle
+// cycles (the causal build fits 168 VGPRs, spilling one value used only at
+// the start and in the epilogue); the non-causal build would spill in its tile
+// loop at that bound and keeps two.
+__global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c0, uint32_t qflip) {
