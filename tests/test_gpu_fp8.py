@@ -59,6 +59,29 @@ def test_fp8_kernel_vs_dequantised_oracle(gpu, N, causal, hadamard):
     assert e_lse <= 1e-3
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_scores_jump_between_tiles(gpu, causal):
+    # Keys scaled up in steps along the sequence (x1, x4, x16): the reference
+    # maximum of the softmax moves in the middle of rows, by more than its
+    # slack, and the P operand must stay inside E4M3 range throughout.
+    w = custom(1, 2, 1500, 128, causal, "fp8", seed=91)
+    q, k, v = make_qkv(w)
+    g = torch.ones(1500)
+    g[300:700] = 4.0
+    g[700:] = 16.0
+    k = (k.float() * g[None, None, :, None]).to(torch.bfloat16)
+    o, lse, (q8, k8, v8, qs, ks, vs) = fp8_run(q, k, v, causal, w.scale, False)
+    o_ref, lse_ref = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, causal, quantize_p=False)
+    o_emu, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, causal, quantize_p=True)
+    e_ref, e_emu = rel_rmse(o, o_ref), rel_rmse(o, o_emu)
+    e_lse = float((np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max())
+    log(f"  causal={causal}: rel RMSE vs fp64 {e_ref:.4f}, vs P-emulation {e_emu:.4f}, LSE {e_lse:.2e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert e_ref <= 3e-2
+    assert e_emu <= 1.5e-2
+    assert e_lse <= 1e-3
+
+
 def test_fp8_single_token_returns_v(gpu):
     w = custom(2, 3, 1, 128, True, "fp8", seed=5)
     q, k, v = make_qkv(w)
