@@ -106,8 +106,9 @@ def cpu_baseline(w, q, k, v, budget_s: float, do=None):
     """Time the float64 oracle on whole heads of the workload until about budget_s
     (for the backward workload: oracle.attention_bwd with the upstream gradient do)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle
+    threadpool_limits(len(os.sched_getaffinity(0)), user_api="blas")   # one BLAS thread per usable core
     qn = q.float().numpy().astype(np.float64)
     kn = k.float().numpy().astype(np.float64)
     vn = v.float().numpy().astype(np.float64)
@@ -129,10 +130,12 @@ def cpu_baseline(w, q, k, v, budget_s: float, do=None):
         done += 1
         if t_used >= budget_s:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    cores = len(os.sched_getaffinity(0))
     value = done * per_head / t_used / (1e9 if decode else 1e12)
-    return {"value": value, "unit": "GB/s" if decode else "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (batch, head) pairs, full rows, float64, {t_used:.1f} s"}
+    return {"value": value, "unit": "GB/s" if decode else "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) pairs, full rows, float64, {t_used:.1f} s, "
+                      f"{blas} BLAS threads"}
 
 
 def main() -> int:
@@ -255,6 +258,7 @@ def main() -> int:
     achieved = work / (kern_avg_ms * 1e-3)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, kernel_source(w))}
+    eprint("[bench] launch times (ms): " + " ".join(f"{t:.4f}" for t in kern_ms))
     eprint(f"[bench] {w.name}: step {ms_per_step:.4f} ms, attention launch(es) avg {kern_avg_ms:.4f} ms "
            f"(min {min(kern_ms):.4f}), {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of {peak} peak")
 

@@ -28,21 +28,25 @@ Readings where the pages are silent:
     zero; the last block covers the remaining rows only; code = E4M3(y / s);
     the scale is stored as float32 (s rounded once from float64) and
     dequantisation is code * s;
-  - the rounding decision y / s -> code is taken in float32, the precision of
-    the quantiser kernel: with y_u = x H (the unnormalised +-1 matrix, exact in
-    float64 for these inputs) and A = max |y_u| over the block, the 1/sqrt(d)
-    cancels and y / s = 448 y_u / A, formed as RN32(RN32(y_u) * RN32(448 /
-    RN32(A))) (then + 0, so a zero quotient is +0); exact E4M3 ties are common
-    (for example y_u = 0.9375 in a block with amax 20 gives exactly 21), so
-    both sides must round the same float32 quotient;
+  - the rounding decision is the definition itself, taken as exactly as
+    float64 allows: with y_u = x H (the +-1 matrix; exact in float64 for bf16
+    inputs) and A = max |y_u| over the block, the 1/sqrt(d) of the orthonormal
+    matrix cancels and y / s is the real number 448 y_u / A, formed by one
+    float64 division of exact operands (so an exact E4M3 tie, for example
+    y_u = 0.9375 in a block whose maximum is 20, which scales to exactly 21,
+    stays a tie and goes to the even code); the quantiser kernel decides in its
+    own float32 arithmetic, so near a rounding boundary either neighbour is a
+    valid code, and the tests check that against the float64 quotient this
+    module returns (quotients());
   - V is quantised per block the same way, without the Hadamard matrix;
   - inside attention P is quantised too (both products run on FP8 matrix
-    cores), with the per-block V scales folded into it: with
-    r_j = s_v(block of key j) / max over blocks of s_v (so 0 < r_j <= 1),
-    P_j is stored as E4M3(256 p_j r_j) and stands for E4M3(256 p_j r_j) /
-    (256 r_j); p = exp(S - m) relative to the row maximum, so 256 p r <= 256
-    stays inside E4M3 range and the power-of-two 256 keeps small p away from
-    the subnormals; the row sum l uses the unquantised p.
+    cores), jointly with the V scale of its key's block: write s_v(j) =
+    2^E_j r_j with E_j = ceil(log2 s_v(j)), so 1/2 < r_j <= 1; P_j is stored as
+    E4M3(256 p_j r_j) and stands for E4M3(256 p_j r_j) / (256 r_j) (the power
+    of two 2^E_j is exact and travels separately); p = exp(S - m) relative to
+    the row maximum, so 256 p r <= 256 stays inside E4M3 range, and the factor
+    256 keeps small p away from the subnormals; the row sum l uses the
+    unquantised p.
 """
 from __future__ import annotations
 
@@ -99,27 +103,46 @@ def e4m3_encode(x) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def quantize_blocks(x, hadamard: bool, block: int = BLOCK):
-    """Incoherent processing (optional) then per-block FP8 quantisation of a
-    [B, H, N, d] tensor.  Returns (codes uint8 [B,H,N,d], scales float32
-    [B,H,ceil(N/block)])."""
+def quotients(x, hadamard: bool, block: int = BLOCK):
+    """The per-block quantisation quotients y / s of a [B, H, N, d] tensor, in
+    float64, and the block maxima A = max |y_u| (y_u = x H with the +-1 matrix,
+    or x without the transform).  Returns (t [B,H,N,d], A [B,H,ceil(N/block)]);
+    t is 0 in an all-zero block."""
     x = np.asarray(x, dtype=np.float64)
     B, H, N, d = x.shape
     yu = x @ sylvester_hadamard(d) if hadamard else x          # y = yu / sqrt(d)
-    norm = E4M3_MAX * np.sqrt(float(d)) if hadamard else E4M3_MAX
     nb = -(-N // block)
-    codes = np.empty((B, H, N, d), dtype=np.uint8)
-    scales = np.empty((B, H, nb), dtype=np.float32)
+    t = np.zeros((B, H, N, d))
+    amax = np.empty((B, H, nb))
     for j in range(nb):
         blk = yu[:, :, j * block:(j + 1) * block, :]
-        amax_u = np.abs(blk).max(axis=(2, 3))                  # amax = amax_u / sqrt(d)
-        a32 = amax_u.astype(np.float32)
-        with np.errstate(divide="ignore"):
-            inv32 = np.where(a32 > 0, np.float32(E4M3_MAX) / a32, np.float32(0)).astype(np.float32)
-        q32 = blk.astype(np.float32) * inv32[:, :, None, None] + np.float32(0)
-        codes[:, :, j * block:(j + 1) * block, :] = e4m3_encode(q32)
-        scales[:, :, j] = np.where(amax_u > 0, amax_u / norm, 1.0).astype(np.float32)
-    return codes, scales
+        a = np.abs(blk).max(axis=(2, 3))
+        amax[:, :, j] = a
+        with np.errstate(divide="ignore", invalid="ignore"):
+            tj = (E4M3_MAX * blk) / a[:, :, None, None]         # y / s = 448 y_u / A, one rounding
+        t[:, :, j * block:(j + 1) * block, :] = np.where(a[:, :, None, None] > 0, tj, 0.0)
+    return t, amax
+
+
+def quantize_blocks(x, hadamard: bool, block: int = BLOCK):
+    """Incoherent processing (optional) then per-block FP8 quantisation of a
+    [B, H, N, d] tensor: code = E4M3(y / s), s = amax / 448 (1 for an all-zero
+    block).  Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)])."""
+    d = np.shape(x)[-1]
+    t, amax_u = quotients(x, hadamard, block)
+    norm = E4M3_MAX * np.sqrt(float(d)) if hadamard else E4M3_MAX   # s = amax_u / (448 sqrt(d))
+    scales = np.where(amax_u > 0, amax_u / norm, 1.0).astype(np.float32)
+    return e4m3_encode(t), scales
+
+
+def pow2_split(s):
+    """s = 2^E r with E = ceil(log2 s) and 1/2 < r <= 1, for positive finite s.
+    Returns (E int64, r float64); both exact."""
+    s = np.asarray(s, dtype=np.float64)
+    m, e = np.frexp(s)                          # s = m 2^e, 1/2 <= m < 1
+    exact = m == 0.5                            # s is a power of two: E = log2 s, r = 1
+    E = np.where(exact, e - 1, e).astype(np.int64)
+    return E, np.where(exact, 1.0, m)
 
 
 def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
@@ -132,8 +155,8 @@ def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
 def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p: bool = True,
                   block: int = BLOCK):
     """Attention on dequantised FP8 operands, with P itself quantised as
-    E4M3(256 p r)/(256 r) when ``quantize_p`` (r: the key's V-block scale over
-    the largest V-block scale of the head; l from the unquantised p).
+    E4M3(256 p r)/(256 r) when ``quantize_p`` (r: the mantissa part in (1/2, 1]
+    of the key's V-block scale, see pow2_split; l from the unquantised p).
     Returns (O, LSE) in float64."""
     q = dequantize_blocks(q8, qs, block)
     k = dequantize_blocks(k8, ks, block)
@@ -152,7 +175,7 @@ def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p
             p = np.exp(s - m)
             l = p.sum(axis=1, keepdims=True)
             if quantize_p:
-                r = np.repeat(vs64[b, h] / vs64[b, h].max(), block)[:N][None, :]
+                r = np.repeat(pow2_split(vs64[b, h])[1], block)[:N][None, :]
                 pq = e4m3_decode(e4m3_encode(256.0 * p * r)) / (256.0 * r)
             else:
                 pq = p

@@ -61,3 +61,63 @@ def compare_sampled(q, k, v, o, lse, causal, scale, kind, heads, rows):
         e = compare(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], o_ref, lse_ref, kind)
         worst = (max(worst[0], e[0]), max(worst[1], e[1]))
     return worst
+
+
+# ---------------------------------------------------------------------------
+# FP8 quantiser codes against the float64 definition
+U32 = 2.0 ** -24     # unit roundoff of float32
+
+
+def fp8_code_margins(x, hadamard):
+    """The quantiser's float32 error bound, per element, in units of the quotient
+    y / s: the transform is formed with float32 butterflies (log2 d stages, each
+    adding at most U32 times the row's l1 norm), the block maximum from those
+    values, and the quotient by one float32 multiply of float32 operands.
+    Returns (oracle quotients t, block maxima A, margins eps)."""
+    xn = np.asarray(x, dtype=np.float64)
+    B, H, N, d = xn.shape
+    t, A = oracle.quotients(xn, hadamard)
+    stages = int(np.log2(d)) if hadamard else 0
+    e_row = stages * U32 * np.abs(xn).sum(axis=3) * 1.01            # [B,H,N] transform error bound
+    nb = A.shape[2]
+    e_blk = np.zeros_like(A)
+    for j in range(nb):
+        e_blk[:, :, j] = e_row[:, :, 128 * j:128 * (j + 1)].max(axis=2)
+    Ar = np.repeat(A, 128, axis=2)[:, :, :N]
+    er = np.repeat(e_blk, 128, axis=2)[:, :, :N]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        eps = np.where(Ar[..., None] > 0,
+                       (448.0 * e_row[..., None] + np.abs(t) * er[..., None]) / Ar[..., None] + 4 * U32 * np.abs(t),
+                       0.0)
+    return t, A, eps
+
+
+def check_fp8_codes(x, codes, scales, hadamard):
+    """Every code must be a valid rounding of the float64 quotient within the
+    kernel's float32 margin: its value lies between the E4M3 roundings of t - eps
+    and t + eps (so either neighbour of a rounding boundary is accepted, and +0
+    and -0 compare equal).  Scales agree with the float64 definition to the
+    same margin.  Returns the number of codes whose value differs from the
+    oracle's code."""
+    xn = f64(x)
+    t, A, eps = fp8_code_margins(xn, hadamard)
+    rc, rs = oracle.quantize_blocks(xn, hadamard)
+    val = oracle.e4m3_decode(codes)
+    lo = oracle.e4m3_decode(oracle.e4m3_encode(t - eps))
+    hi = oracle.e4m3_decode(oracle.e4m3_encode(t + eps))
+    ok = (val >= lo) & (val <= hi)
+    bad = int((~ok).sum())
+    assert bad == 0, f"{bad} codes outside the valid rounding interval"
+    ndiff = int((val != oracle.e4m3_decode(rc)).sum())
+    nb = A.shape[2]
+    e_blk = np.zeros_like(A)
+    if hadamard:
+        e_row = int(np.log2(xn.shape[3])) * U32 * np.abs(xn).sum(axis=3) * 1.01
+        for j in range(nb):
+            e_blk[:, :, j] = e_row[:, :, 128 * j:128 * (j + 1)].max(axis=2)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(A > 0, e_blk / A, 0.0) + 2 * U32
+    sg, so = scales.astype(np.float64), rs.astype(np.float64)
+    assert np.all(np.abs(sg - so) <= rel * so), "block scales differ from amax / 448 beyond the float32 margin"
+    assert np.all(sg[A == 0] == 1.0)
+    return ndiff

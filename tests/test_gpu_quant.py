@@ -1,6 +1,8 @@
-"""GPU parity of the Hadamard + per-block E4M3 quantiser: codes bit-exact and
-scales equal to the oracle's (both take the rounding decision on the same
-float32 quotient; the transform itself is exact)."""
+"""GPU parity of the Hadamard + per-block E4M3 quantiser against the float64
+definition code = E4M3(y / s), s = amax / 448.  The kernel decides in float32,
+so a code is accepted when it is a valid rounding of the exact quotient within
+the kernel's stated float32 margin (check_fp8_codes); the number of codes that
+differ from the oracle's is reported and bounded."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import io_aware_exact_16_amd as fa
 import oracle
 from io_aware_exact_16_amd.workloads import WORKLOADS, custom, make_qkv
 
-from gpu_helpers import f64, log
+from gpu_helpers import check_fp8_codes, log
 
 pytestmark = pytest.mark.gpu
 
@@ -21,31 +23,40 @@ def _quant(x, hadamard):
     return x8.cpu().numpy(), s.cpu().numpy()
 
 
-def _exact(x, hadamard):
+def _valid(x, hadamard, tag=""):
     codes, scales = _quant(x, hadamard)
-    rc, rs = oracle.quantize_blocks(f64(x), hadamard)
-    mism = int((codes != rc).sum())
-    assert mism == 0, f"{mism} codes differ from the oracle"
-    np.testing.assert_array_equal(scales, rs)
+    ndiff = check_fp8_codes(x, codes, scales, hadamard)
+    log(f"  {tag} hadamard={hadamard}: {ndiff} of {codes.size} codes differ from the oracle "
+        f"({100.0 * ndiff / max(codes.size, 1):.4f} %), all within the float32 margin")
+    assert ndiff <= 1e-3 * codes.size + 1
+    return ndiff
 
 
 @pytest.mark.parametrize("hadamard", [False, True])
 @pytest.mark.parametrize("N", [1, 100, 128, 300, 1000])
-def test_bf16_codes_exact(gpu, N, hadamard):
+def test_bf16_codes_valid(gpu, N, hadamard):
     q, _, _ = make_qkv(custom(2, 3, N, 128, True, "fp8", seed=N + 1, outlier_frac=0.001))
-    _exact(q, hadamard)
+    _valid(q, hadamard, f"N={N}")
 
 
 @pytest.mark.parametrize("hadamard", [False, True])
-def test_fp32_input_codes_exact(gpu, hadamard):
+def test_fp32_input_codes_valid(gpu, hadamard):
     g = torch.Generator().manual_seed(21)
     x = torch.randn(1, 2, 260, 128, generator=g)
-    _exact(x, hadamard)
+    _valid(x, hadamard, "fp32")
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_fp32_input_wide_exponent_spread(gpu, hadamard):
+    # rows mixing magnitudes 2^-30 .. 2^10: float32 sums are no longer exact
+    g = torch.Generator().manual_seed(22)
+    x = torch.randn(1, 2, 256, 128, generator=g) * torch.exp2(torch.randint(-30, 11, (1, 2, 256, 128), generator=g))
+    _valid(x, hadamard, "fp32 wide spread")
 
 
 def test_d64_without_hadamard(gpu):
     q, _, _ = make_qkv(custom(1, 4, 333, 64, False, "bf16", seed=22))
-    _exact(q, False)
+    _valid(q, False, "d=64")
 
 
 @pytest.mark.parametrize("hadamard", [False, True])
@@ -54,7 +65,7 @@ def test_fp8_workload_full_size(gpu, hadamard):
     q, k, v = make_qkv(w)
     for name, x, had in (("q", q, hadamard), ("k", k, hadamard), ("v", v, False)):
         log(f"[{w.name}] quantise {name} hadamard={had}")
-        _exact(x, had)
+        _valid(x, had, f"{w.name} {name}")
 
 
 def test_transform_of_basis_rows_is_hadamard_sign_pattern(gpu):
@@ -66,12 +77,24 @@ def test_transform_of_basis_rows_is_hadamard_sign_pattern(gpu):
     assert scales[0, 0, 0] == np.float32(1.0 / (448.0 * np.sqrt(128.0)))
 
 
+def test_exact_ties_with_hadamard(gpu):
+    # x = 20 H[3] + 0.9375 H[70] scales coordinate 70 to exactly 21 (a tie between
+    # 20 and 22, to the even code 20); float32 butterflies are exact on these values
+    h = torch.from_numpy(oracle.sylvester_hadamard(128))
+    x = torch.zeros(1, 1, 128, 128, dtype=torch.float32)
+    x[0, 0, 0] = 20.0 * h[3] + 0.9375 * h[70]
+    x[0, 0, 1] = -x[0, 0, 0]
+    codes, _ = _quant(x, True)
+    assert oracle.e4m3_decode(codes[0, 0, 0, 70]) == 20.0 and oracle.e4m3_decode(codes[0, 0, 1, 70]) == -20.0
+    _valid(x, True, "ties")
+
+
 def test_zero_block_has_unit_scale(gpu):
     x = torch.zeros(1, 1, 200, 128, dtype=torch.bfloat16)
     x[0, 0, 150:] = 1.0
     codes, scales = _quant(x, True)
-    assert scales[0, 0, 0] == 1.0 and np.all(codes[0, 0, :128] == 0)
-    _exact(x, True)
+    assert scales[0, 0, 0] == 1.0 and np.all(codes[0, 0, :128] & 0x7F == 0)
+    _valid(x, True, "zero block")
 
 
 def test_deterministic(gpu):

@@ -5,6 +5,7 @@ CPU only."""
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -417,22 +418,96 @@ def test_quantize_blocks_properties():
                     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("outliers", [False, True])
-def test_quantize_blocks_without_hadamard_is_torch_cast_of_scaled(outliers):
-    # torch computes the same float32 quotient x * (448 / amax) and casts it
-    g = torch.Generator().manual_seed(3)
+def _e4m3_grid():
+    """Every finite E4M3 value with its code, from the bit layout written out
+    by hand: exponent field e (bias 7), mantissa field m; e = 0 is subnormal."""
+    vals = []
+    for sign in (0, 1):
+        for e in range(16):
+            for m in range(8):
+                if e == 15 and m == 7:
+                    continue                                   # NaN
+                mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+                vals.append((-mag if sign else mag, (sign << 7) | (e << 3) | m))
+    return vals
+
+
+def _nearest_e4m3_exact(t: Fraction) -> int:
+    """Round an exact rational to E4M3 by exhaustive search: the nearest finite
+    value, ties to the even code (mantissa bit 0), magnitudes beyond 448 to 448."""
+    grid = _nearest_e4m3_exact.grid
+    best = min(abs(v - t) for v, _ in grid)
+    cands = [(v, c) for v, c in grid if abs(v - t) == best]
+    if len(cands) > 1:
+        cands = [(v, c) for v, c in cands if v != 0 or (c & 0x80) == ((t < 0) << 7)] or cands
+        even = [(v, c) for v, c in cands if c & 1 == 0]
+        cands = even or cands
+    return cands[0][1]
+
+
+_nearest_e4m3_exact.grid = _e4m3_grid()
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_quantize_codes_are_exact_nearest_e4m3(hadamard):
+    # bf16 inputs with +-20 outliers: for sampled elements the exact rational
+    # y / s = 448 y_u / A (y_u = x H summed in exact rationals) is rounded to
+    # E4M3 by exhaustive search over all finite codes; the oracle must agree.
+    g = torch.Generator().manual_seed(3 + hadamard)
     x = torch.randn(1, 2, 256, 128, generator=g)
-    if outliers:
-        m = torch.rand(x.shape, generator=g) < 0.001
-        x[m] = 20.0
-    x = x.to(torch.bfloat16).float()
-    codes, scales = oracle.quantize_blocks(x.double().numpy(), False)
-    for j in range(2):
-        blk = x[:, :, j * 128:(j + 1) * 128]
-        amax = blk.abs().amax(dim=(2, 3), keepdim=True)
-        ref = (blk * (448.0 / amax)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        np.testing.assert_array_equal(codes[:, :, j * 128:(j + 1) * 128], ref)
-        np.testing.assert_array_equal(scales[:, :, j], (amax[:, :, 0, 0].double() / 448.0).float().numpy())
+    m = torch.rand(x.shape, generator=g) < 0.001
+    x[m] = 20.0 * (torch.randint(0, 2, x.shape, generator=g)[m] * 2.0 - 1.0)
+    x = x.to(torch.bfloat16).double().numpy()
+    codes, scales = oracle.quantize_blocks(x, hadamard)
+    h = [[1 if bin(i & j).count("1") % 2 == 0 else -1 for j in range(128)] for i in range(128)]   # H[i][j]
+    r = np.random.default_rng(7)
+    for hh in range(2):
+        for j in range(2):
+            blk = x[0, hh, 128 * j:128 * (j + 1)]
+            fr = [[Fraction(float(v)) for v in row] for row in blk]
+            if hadamard:
+                yu = [[sum(fr[t][k] * h[k][i] for k in range(128)) for i in range(128)] for t in range(128)]
+            else:
+                yu = fr
+            A = max(abs(v) for row in yu for v in row)
+            assert scales[0, hh, j] == np.float32(float(A) / (448.0 * (128 ** 0.5 if hadamard else 1.0)))
+            for _ in range(300):
+                t, i = int(r.integers(128)), int(r.integers(128))
+                want = _nearest_e4m3_exact(448 * yu[t][i] / A)
+                assert codes[0, hh, 128 * j + t, i] == want, (hh, j, t, i)
+
+
+def test_quantize_exact_tie_with_hadamard_goes_to_even():
+    # x = 20 H[3] + 0.9375 H[70] (rows of the +-1 matrix) gives y_u = x H =
+    # 128 (20 e_3 + 0.9375 e_70): A = 2560 and coordinate 70 scales to exactly
+    # 448 * 120 / 2560 = 21, halfway between the E4M3 values 20 and 22
+    h = oracle.sylvester_hadamard(128)
+    x = np.zeros((1, 1, 128, 128))
+    x[0, 0, 0] = 20.0 * h[3] + 0.9375 * h[70]
+    x[0, 0, 1] = -(20.0 * h[3]) - 0.9375 * h[70]
+    codes, scales = oracle.quantize_blocks(x, True)
+    assert oracle.e4m3_decode(codes[0, 0, 0, 70]) == 20.0 and oracle.e4m3_decode(codes[0, 0, 1, 70]) == -20.0
+    assert codes[0, 0, 0, 3] == 0x7E and codes[0, 0, 1, 3] == 0xFE
+    t, amax = oracle.quotients(x, True)
+    assert t[0, 0, 0, 70] == 21.0 and amax[0, 0, 0] == 2560.0
+
+
+def test_quotients_are_one_rounding_of_the_exact_ratio():
+    x = rng.standard_normal((1, 1, 128, 128)).astype(np.float32).astype(np.float64)
+    t, amax = oracle.quotients(x, False)
+    A = max(abs(Fraction(float(v))) for v in x.ravel())
+    for (i, j) in [(0, 0), (5, 17), (127, 127), (64, 3)]:
+        exact = 448 * Fraction(float(x[0, 0, i, j])) / A
+        assert abs(Fraction(float(t[0, 0, i, j])) - exact) <= abs(exact) * Fraction(2) ** -53
+
+
+def test_pow2_split():
+    s = np.array([1.0, 0.75, 3.0, 2.0 ** -140, 2.0 ** 20, 448.0, 1.0 / 448.0, 5.0e-39, 1e30])
+    E, r = oracle.pow2_split(s)
+    for si, ei, ri in zip(s, E, r):
+        assert 0.5 < ri <= 1.0
+        assert math.ldexp(float(ri), int(ei)) == float(si)
+        assert ei == math.ceil(math.log2(float(si))) or (si == 5.0e-39)   # log2 of a subnormal may round
 
 
 def test_quantize_exact_tie_goes_to_even():
@@ -480,26 +555,25 @@ def test_attention_fp8_without_p_quant_is_plain_attention():
 
 
 def test_attention_fp8_p_quant_error_bound():
-    # each quantised p is within 2^-4 relative (normals) or 2^-10/(256 r) absolute
-    # (subnormals of 256 p r); here every V block has the same scale, so r = 1
+    # each quantised p is within 2^-4 relative (normal range of 256 p r) or
+    # 2^-10 / (256 r) <= 2^-17 absolute (subnormals; r > 1/2), so
+    # |O_q - O| <= (2^-4 + N 2^-17 / l) max|V| with l >= 1
     shape = (1, 1, 256, 128)
     q, k, v = (rng.standard_normal(shape) for _ in range(3))
+    v[:, :, 128:] *= 3.0                                   # unequal V-block scales
     q8, qs = oracle.quantize_blocks(q, False)
     k8, ks = oracle.quantize_blocks(k, False)
     v8, vs = oracle.quantize_blocks(v, False)
     o_q, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, False, quantize_p=True)
     o_n, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, False, quantize_p=False)
     vmax = np.abs(oracle.dequantize_blocks(v8, vs)).max()
-    vs_eq = np.full_like(vs, vs.max())
-    o_q, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs_eq, 128 ** -0.5, False, quantize_p=True)
-    o_n, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs_eq, 128 ** -0.5, False, quantize_p=False)
-    assert np.abs(o_q - o_n).max() <= (2.0 ** -4 + 256 * 2.0 ** -18) * vmax * (vs_eq.max() / vs.min())
+    assert np.abs(o_q - o_n).max() <= (2.0 ** -4 + 256 * 2.0 ** -17) * vmax
     assert np.abs(o_q - o_n).max() > 0
 
 
 def test_attention_fp8_p_quant_folds_v_block_scales():
-    # with unequal V-block scales, P is quantised as E4M3(256 p r)/(256 r): check
-    # one row against a scalar loop over its keys
+    # with unequal V-block scales, P is quantised as E4M3(256 p r)/(256 r) with r
+    # the block scale over the next power of two up: one row against a scalar loop
     shape = (1, 1, 256, 128)
     q, k, v = (rng.standard_normal(shape) for _ in range(3))
     v[:, :, 128:] *= 3.0                                   # second V block has a larger scale
@@ -513,10 +587,28 @@ def test_attention_fp8_p_quant_folds_v_block_scales():
     p = np.exp(srow - srow.max())
     num = np.zeros(128)
     for j in range(256):
-        r = float(vs[0, 0, j // 128]) / float(vs[0, 0].max())
+        sv = float(vs[0, 0, j // 128])
+        r = sv / 2.0 ** math.ceil(math.log2(sv))
         pq = float(oracle.e4m3_decode(oracle.e4m3_encode(256.0 * p[j] * r))) / (256.0 * r)
         num += pq * vd[0, 0, j]
     np.testing.assert_allclose(o[0, 0, i], num / p.sum(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("std", [1.0, 1e-2, 1e-3])
+def test_attention_fp8_p_quant_with_a_zero_v_block(std):
+    # an all-zero V block gets the unit scale; the other blocks' P must keep its
+    # relative precision whatever V's magnitude (each block's fold is its own)
+    shape = (1, 2, 384, 128)
+    q, k, v = (rng.standard_normal(shape) for _ in range(3))
+    v = v * std
+    v[:, :, 256:] = 0.0
+    q8, qs = oracle.quantize_blocks(q, False)
+    k8, ks = oracle.quantize_blocks(k, False)
+    v8, vs = oracle.quantize_blocks(v, False)
+    assert np.all(vs[:, :, 2] == 1.0)
+    o_q, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, True, quantize_p=True)
+    o_n, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, 128 ** -0.5, True, quantize_p=False)
+    assert np.linalg.norm(o_q - o_n) / np.linalg.norm(o_n) <= 3e-2
 
 
 def test_fp8_incoherent_processing_helps_on_channel_outliers():
@@ -534,7 +626,9 @@ def test_fp8_incoherent_processing_helps_on_channel_outliers():
         v8, vs = oracle.quantize_blocks(v, False)
         o, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, True)
         errs[had] = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
-    assert errs[True] <= 6e-2 and errs[False] >= 2.0 * errs[True], errs
+    # the pages' claim is the ratio (~2.6x lower error); 8e-2 is a regression bound
+    # (the 6e-2 bound is stated for the sparse-outlier workload, not this one)
+    assert errs[True] <= 8e-2 and errs[False] >= 2.0 * errs[True], errs
 
 
 def test_fp8_variants_study():
