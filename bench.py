@@ -5,8 +5,9 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input
 that is already resident in HBM: for the bf16/fp32 workloads one fa_fwd call;
-for the FP8 workload the three Hadamard/FP8 quantiser calls (Q and K with the
-transform, V without) followed by fa_fwd_fp8; for the decode workload one
+for the FP8 workload one fa_qkv_fp8_quant launch (Hadamard transform and
+per-block FP8 quantisation of Q and K, V quantised without the transform and
+with power-of-two block scales) followed by fa_fwd_fp8; for the decode workload one
 fa_fwd_decode call (split-KV kernel + merge); for the backward workload one
 fa_bwd call (Delta pass, dK/dV kernel, dQ kernel), with the forward's O and
 LSE computed once beforehand.  W untimed steps, then K timed
@@ -180,9 +181,7 @@ def main() -> int:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
         def step(record=None):
-            fa.fa_hadamard_fp8_quant(qd, q8, qs, True)
-            fa.fa_hadamard_fp8_quant(kd, k8, ks, True)
-            fa.fa_hadamard_fp8_quant(vd, v8, vs, False)
+            fa.fa_qkv_fp8_quant(qd, kd, vd, q8, k8, v8, qs, ks, vs, fa.FA_QUANT_HADAMARD_QK | fa.FA_QUANT_POW2_SCALE_V)
             if record is not None:
                 record[0].record(stream)
             fa.fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, w.scale, w.causal)

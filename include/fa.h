@@ -104,7 +104,10 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * fa_hadamard_fp8_quant -- incoherent processing and per-block FP8 quantisation.
+ * fa_hadamard_fp8_quant -- incoherent processing and per-block FP8 quantisation
+ * ("FlashAttention-3 (PT)", section "Inovacoes tecnicas", item 3: Q and K are
+ * multiplied by an orthogonal matrix, for example a Hadamard matrix, before
+ * FP8 quantisation, which spreads outliers; the matrix cancels in Q K^T).
  *   x        : [B,H,N,d] input, in_dtype FA_BF16 or FA_F32.
  *   x8       : [B,H,N,d] E4M3 output bytes.
  *   scales   : [B,H,ceil(N/128)] float32 output block scales.
@@ -113,11 +116,41 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  *              (any d in {64,128}).
  * Per block of 128 tokens (fewer in the last block): amax = max |y| over the
  * block, s = amax / 448 (s = 1 when amax = 0), code = E4M3 round-to-nearest-even
- * of y / s.  The transform is computed exactly (float64 butterflies), so the
- * codes do not depend on summation order.
+ * of y / s.  The transform and the quotient are formed in float32 (butterfly
+ * error at most log2(d) 2^-24 times the row's l1 norm), so a quotient that lies
+ * within that error of an E4M3 rounding boundary may go to either neighbour;
+ * all other codes are the correctly rounded E4M3 of y / s.  One head of x must
+ * be below 4 GiB (N d sizeof(element) < 2^32), else FA_ERR_SHAPE.
  */
 int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scales,
                           int B, int H, int N, int d, int hadamard, void* stream);
+
+/* Flags of fa_qkv_fp8_quant. */
+enum fa_quant_flags {
+  FA_QUANT_HADAMARD_QK = 1,   /* Q and K through the normalised Hadamard transform first */
+  FA_QUANT_HADAMARD_V = 2,    /* V through it too */
+  FA_QUANT_POW2_SCALE_V = 4   /* V's block scale is the power of two 2^ceil(log2(amax / 448)) (at least
+                                 2^-126): the E8M0 form, which fa_fwd_fp8 applies exactly in its matrix
+                                 instruction, so the V scale never rounds inside P */
+};
+
+/*
+ * fa_qkv_fp8_quant -- per-block FP8 quantisation of Q, K and V of one attention
+ * call in a single launch (same passage as fa_hadamard_fp8_quant).
+ *   q, k, v        : [B,H,N,128] inputs, in_dtype FA_BF16 or FA_F32.
+ *   q8, k8, v8     : [B,H,N,128] E4M3 outputs;  q_scale, k_scale, v_scale :
+ *                    [B,H,ceil(N/128)] float32 outputs.
+ *   d              : must be 128.
+ *   flags          : an OR of fa_quant_flags (other bits: FA_ERR_ARG).
+ * Q and K: as fa_hadamard_fp8_quant(hadamard = FA_QUANT_HADAMARD_QK set).  V: the
+ * same with its own transform flag; with FA_QUANT_POW2_SCALE_V its scale is
+ * s = 2^E, E = ceil(log2(amax / 448)), code = E4M3(y / s) (without the
+ * transform y / s = x 2^-E is exact, so every code is the correctly rounded
+ * one).  No output may equal an input or another output (FA_ERR_ARG).
+ */
+int fa_qkv_fp8_quant(const void* q, const void* k, const void* v, int in_dtype, uint8_t* q8, uint8_t* k8,
+                     uint8_t* v8, float* q_scale, float* k_scale, float* v_scale, int B, int H, int N, int d,
+                     int flags, void* stream);
 
 /*
  * Split-KV forward for a few queries against a long key sequence (a decode

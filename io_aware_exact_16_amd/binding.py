@@ -22,7 +22,8 @@ FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
                 -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG"}
-EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_fwd_decode_workspace_bytes", "fa_fwd_decode",
+EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_qkv_fp8_quant", "fa_fwd_decode_workspace_bytes",
+            "fa_fwd_decode",
             "fa_lse_merge", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string")
 BLOCK = 128   # tokens per FP8 scaling block
 
@@ -52,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = I
     lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
     lib.fa_hadamard_fp8_quant.restype = I
+    lib.fa_qkv_fp8_quant.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.fa_qkv_fp8_quant.restype = I
     lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
@@ -146,6 +149,30 @@ def fa_hadamard_fp8_quant(x, x8, scales, hadamard: bool) -> None:
     _check("fa_hadamard_fp8_quant", st)
 
 
+FA_QUANT_HADAMARD_QK, FA_QUANT_HADAMARD_V, FA_QUANT_POW2_SCALE_V = 1, 2, 4
+
+
+def fa_qkv_fp8_quant(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, flags: int) -> None:
+    """q8, k8, v8 (uint8 E4M3) and their block scales <- per-block quantisation of q, k, v
+    (bf16 or fp32, [B,H,N,128]) in one launch; ``flags`` is an OR of FA_QUANT_HADAMARD_QK,
+    FA_QUANT_HADAMARD_V and FA_QUANT_POW2_SCALE_V."""
+    code = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(q.dtype)
+    if code is None:
+        raise ValueError(f"fa_qkv_fp8_quant: unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev4(name, t, q.dtype, (B, H, N, d))
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _dev4(name, t, torch.uint8, (B, H, N, d))
+    nb = -(-N // BLOCK)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and tuple(t.shape) == (B, H, nb)):
+            raise ValueError(f"fa_qkv_fp8_quant: {name} must be a contiguous float32 CUDA tensor [B,H,{nb}]")
+    st = load().fa_qkv_fp8_quant(_ptr(q), _ptr(k), _ptr(v), code, _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+                                 _ptr(k_scale), _ptr(v_scale), B, H, N, d, int(flags), _stream(q))
+    _check("fa_qkv_fp8_quant", st)
+
+
 def fa_fwd_decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
     """Device workspace (bytes) fa_fwd_decode needs; 0 for invalid sizes.  No GPU needed."""
     return int(load().fa_fwd_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
@@ -232,6 +259,18 @@ def quant_fp8(x, hadamard: bool = True):
     scales = torch.empty((B, H, -(-N // BLOCK)), dtype=torch.float32, device=x.device)
     fa_hadamard_fp8_quant(x, x8, scales, hadamard)
     return x8, scales
+
+
+def quant_qkv_fp8(q, k, v, hadamard_qk: bool = True, hadamard_v: bool = False, pow2_v: bool = True):
+    """Return ((q8, qs), (k8, ks), (v8, vs)) from one fa_qkv_fp8_quant launch (by default
+    the FP8 attention path: Q and K transformed, V with a power-of-two block scale)."""
+    B, H, N, d = q.shape
+    xs = [torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device) for _ in range(3)]
+    ss = [torch.empty((B, H, -(-N // BLOCK)), dtype=torch.float32, device=q.device) for _ in range(3)]
+    flags = ((FA_QUANT_HADAMARD_QK if hadamard_qk else 0) | (FA_QUANT_HADAMARD_V if hadamard_v else 0)
+             | (FA_QUANT_POW2_SCALE_V if pow2_v else 0))
+    fa_qkv_fp8_quant(q, k, v, *xs, *ss, flags)
+    return tuple(zip(xs, ss))
 
 
 def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None):

@@ -424,13 +424,9 @@ hipError_t launch_attn_bf16_pp(const void* q, const void* k, const void* v, void
   const int nqb = (N + BR - 1) / BR;
   const int BH = B * H;
   const int total = nqb * BH;
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_pp_kernel, NT, 0);
-  if (e != hipSuccess) return e;
   // one persistent workgroup per resident slot, never more than there are items
-  const long slots = (long)cus * (per_cu > 0 ? per_cu : 1);
+  const long slots = device_slots(reinterpret_cast<const void*>(&attn_fwd_bf16_pp_kernel), NT);
+  if (slots <= 0) return hipErrorInvalidDevice;
   int grid = total < slots ? total : (int)slots;
   int groups = 1;
   if (BH % 8 == 0 && grid >= 8) {            // one head set per XCD

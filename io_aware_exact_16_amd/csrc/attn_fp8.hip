@@ -10,11 +10,17 @@
 //  * S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales)
 //    over the codes; the two block scales fold into the softmax constant of
 //    the tile: c_t = |scale| log2(e) s_q s_k.
-//  * P is quantised to E4M3 for the second product as 256 p r_t with
-//    r_t = s_v(tile) / max_blocks s_v: the V-block scale rides in P, so one
-//    accumulator serves all V blocks and 256 p r stays in range; the
-//    factor 256 r_t is folded into the exp2 argument (no extra multiply), and
-//    l accumulates p = P / (256 r_t) in float32.  O = acc * max s_v / (256 l).
+//  * P is quantised to E4M3 for the second product jointly with the V-block
+//    scale relative to the head's largest: s_v / max s_v = 2^E r with
+//    E = ceil(log2 of the ratio) and 1/2 < r <= 1; P holds E4M3(256 p r) and
+//    the power of two 2^E goes in as the E8M0 block scale of the V operand of
+//    v_mfma_scale_f32_32x32x64_f8f6f4.  One accumulator serves every V block,
+//    256 p r stays in E4M3's normal range whatever the blocks' magnitudes (an
+//    all-zero block has s_v = 1), and in the block with the largest scale
+//    r = 1, so a row's largest weight is stored exactly.  The factor 256 r is
+//    folded into the exp2 argument (no extra multiply), l accumulates
+//    p = P / (256 r) in float32, and O = acc max s_v / (256 l).  The per-block
+//    constants are formed once per 128-key block (two tiles).
 //  * The reference maximum moves only when a tile's maximum exceeds it by
 //    more than 0.8 in the exp2 domain, so p <= 2^0.8 and 256 p r <= 445.7,
 //    inside E4M3 range (448), and the O rescale is rare.
@@ -67,6 +73,41 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Same product with the A operand's values multiplied by 2^(ea - 127) (E8M0
+// block scale in byte 0 of ea, the same for every lane and 32-element block).
+__device__ __forceinline__ f32x16 mfma_fp8_scaled_a(const i32x8& a, const i32x8& b, const f32x16& c, int ea) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
+}
+
+// Constants of one 128-key block: c_t = softmax constant with the Q and K
+// block scales folded in; lr = log2(256 r); inv_r = 1 / (256 r); ve = E8M0
+// code of 2^E, where s_v / max s_v = 2^E r, 1/2 < r <= 1.  A ratio below
+// 2^-127 leaves part of its magnitude in r, which then loses precision in P's
+// subnormals (such a block's contribution is below 2^-118 of the largest).
+struct BlockK {
+  float c_t, lr, inv_r;
+  int ve;
+};
+
+__device__ __forceinline__ BlockK block_consts(float c_q, float ks, float ratio) {
+  int E;
+  float r = frexpf(ratio, &E);               // ratio = r 2^E, 1/2 <= r < 1
+  if (r == 0.5f) {                           // a power of two: r = 1
+    r = 1.0f;
+    E -= 1;
+  }
+  if (E < -127) {
+    r = ldexpf(r, E + 127);
+    E = -127;
+  }
+  BlockK b;
+  b.c_t = c_q * ks;
+  b.lr = 8.0f + __log2f(r);
+  b.inv_r = 1.0f / (256.0f * r);
+  b.ve = E + 127;
+  return b;
+}
+
 __device__ __forceinline__ float wave_halves_max(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
@@ -86,13 +127,13 @@ constexpr float P_SLACK = 0.8f;   // log2 of the allowed growth of p above 1
 
 constexpr int VMCNT(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
-// One 64-key tile of one wave.  c_t: softmax constant of the tile (block
-// scales folded in); lr: log2(256 r_t); inv_r: 1 / (256 r_t).
+// One 64-key tile of one wave, with the constants of its 128-key block.
 template <bool CAUSAL, bool MASK>
 __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const uint32_t (&koff)[2][2],
                                           const uint32_t (&voff)[4], const i32x8 (&qf)[2], f32x16 (&acc)[4],
-                                          float& m2, float& lsum, float c_t, float lr, float inv_r, int j0, int qi,
-                                          int N, int half) {
+                                          float& m2, float& lsum, const BlockK& bk, int j0, int qi, int N,
+                                          int half) {
+  const float c_t = bk.c_t;
   constexpr int KB_BYTES = 32 * D;   // one 32-key block of the tile
   constexpr int KG_BYTES = 16 * D;   // 16 keys
   f32x16 s[2];
@@ -140,9 +181,9 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
     m2 = mnew;
   }
 
-  // P'' = 256 r_t exp2(c_t s - m2), quantised to E4M3 (round to nearest even);
+  // P'' = 256 r exp2(c_t s - m2), quantised to E4M3 (round to nearest even);
   // the byte for key slot e of the B operand comes from register (e / 16, e % 16)
-  const float off = lr - m2;
+  const float off = bk.lr - m2;
   i32x8 pq;
   float rs[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -158,7 +199,7 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
     uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
     pq[w] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], b, true);
   }
-  lsum += (rs[0] + rs[1]) * inv_r;
+  lsum += (rs[0] + rs[1]) * bk.inv_r;
 
   // O^T += V^T P^T: the A operand for d-block db gathers keys 16g + 8h + 0..7 (g = 0..3)
 #pragma unroll
@@ -170,7 +211,7 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
       va[2 * g] = v[0];
       va[2 * g + 1] = v[1];
     }
-    acc[db] = mfma_fp8(va, pq, acc[db]);
+    acc[db] = mfma_fp8_scaled_a(va, pq, acc[db], bk.ve);
   }
 }
 
@@ -270,32 +311,29 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
   float m2 = -INFINITY, lsum = 0.0f;
 
-  auto step = [&](int t, auto bufc) {
+  auto step = [&](int t, const BlockK& bk, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     const int j0 = t * BC;
     __builtin_amdgcn_s_waitcnt(VMCNT(0));
     __syncthreads();
     if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
     if (CAUSAL && j0 > qw + 31) return;
-    const float ks = ksh[j0 / QBLK], r_t = vsh[j0 / QBLK] / svmax;
-    const float c_t = c_q * ks;
-    const float lr = 8.0f + __log2f(r_t);
-    const float inv_r = 1.0f / (256.0f * r_t);
     const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
     const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
     if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
-      tile_math<CAUSAL, true>(kt, vt, koff, voff, qf, acc, m2, lsum, c_t, lr, inv_r, j0, qi, N, half);
+      tile_math<CAUSAL, true>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half);
     else
-      tile_math<CAUSAL, false>(kt, vt, koff, voff, qf, acc, m2, lsum, c_t, lr, inv_r, j0, qi, N, half);
+      tile_math<CAUSAL, false>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half);
   };
 
   issue_tile(0, IC<0>{});
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, IC<0>{});
-    if (t + 1 < ntiles) step(t + 1, IC<1>{});
+  for (int t = 0; t < ntiles; t += 2) {       // tiles t and t + 1 share one 128-key scaling block
+    const BlockK bk = block_consts(c_q, ksh[t / 2], vsh[t / 2] / svmax);
+    step(t, bk, IC<0>{});
+    if (t + 1 < ntiles) step(t + 1, bk, IC<1>{});
   }
 
-  // epilogue: O = acc * max s_v / (256 l), LSE = ln 2 * (m2 + log2 l)
+  // epilogue: O = acc max s_v / (256 l), LSE = ln 2 * (m2 + log2 l)
   const float ltot = wave_halves_sum(lsum);
   if (qi < N) {
     const float f = svmax / (256.0f * ltot);

@@ -3,6 +3,10 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
@@ -23,6 +27,30 @@ bool sizes_ok(int B, int H, int N, int d, int rows_per_block) {
 int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 }  // namespace
+
+namespace fa {
+
+long device_slots(const void* kernel, int block_threads) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int>, long> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_tuple(dev, kernel, block_threads);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess) return 0;
+  const long slots = (long)cus * (per_cu > 0 ? per_cu : 1);
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = slots;
+  return slots;
+}
+
+}  // namespace fa
 
 extern "C" {
 
@@ -67,9 +95,38 @@ int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scale
   if (hadamard != 0 && hadamard != 1) return FA_ERR_ARG;
   if (d != 128 && !(d == 64 && !hadamard)) return FA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, H, N, d, 128)) return FA_ERR_SHAPE;
+  // one head of the input is addressed with 32-bit byte offsets
+  if ((long long)N * d * (in_dtype == FA_F32 ? 4 : 2) >= (1LL << 32)) return FA_ERR_SHAPE;
   if ((const void*)x8 == x || (const void*)scales == x || (void*)scales == (void*)x8) return FA_ERR_ARG;
   return launch_status(fa::launch_hadamard_fp8_quant(x, in_dtype == FA_BF16, x8, scales, B, H, N, d, hadamard != 0,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+int fa_qkv_fp8_quant(const void* q, const void* k, const void* v, int in_dtype, uint8_t* q8, uint8_t* k8,
+                     uint8_t* v8, float* q_scale, float* k_scale, float* v_scale, int B, int H, int N, int d,
+                     int flags, void* stream) {
+  if (!q || !k || !v || !q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale) return FA_ERR_NULL;
+  if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_DTYPE;
+  if (flags & ~(FA_QUANT_HADAMARD_QK | FA_QUANT_HADAMARD_V | FA_QUANT_POW2_SCALE_V)) return FA_ERR_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, N, d, 128)) return FA_ERR_SHAPE;
+  if ((long long)N * d * (in_dtype == FA_F32 ? 4 : 2) >= (1LL << 32)) return FA_ERR_SHAPE;
+  if ((long long)B * H * ((N + 127) / 128) * 3 > kMaxGrid) return FA_ERR_SHAPE;
+  const void* ins[3] = {q, k, v};
+  void* outs[6] = {q8, k8, v8, q_scale, k_scale, v_scale};
+  for (void* o : outs)
+    for (const void* p : ins)
+      if (o == p) return FA_ERR_ARG;
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (outs[i] == outs[j]) return FA_ERR_ARG;
+  uint8_t* const x8[3] = {q8, k8, v8};
+  float* const sc[3] = {q_scale, k_scale, v_scale};
+  const int hqk = (flags & FA_QUANT_HADAMARD_QK) ? 1 : 0;
+  const int had[3] = {hqk, hqk, (flags & FA_QUANT_HADAMARD_V) ? 1 : 0};
+  const int pow2[3] = {0, 0, (flags & FA_QUANT_POW2_SCALE_V) ? 1 : 0};
+  return launch_status(fa::launch_qkv_fp8_quant(ins, in_dtype == FA_BF16, x8, sc, had, pow2, B, H, N,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 size_t fa_fwd_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {

@@ -44,6 +44,16 @@ hipError_t launch_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* 
 hipError_t launch_hadamard_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8, float* scales,
                                      int B, int H, int N, int d, bool hadamard, hipStream_t stream);
 
+// Q, K and V (d = 128, one shape) in one launch, each with its own transform
+// and power-of-two-scale flags.
+hipError_t launch_qkv_fp8_quant(const void* const x[3], bool x_is_bf16, uint8_t* const x8[3], float* const scales[3],
+                                const int had[3], const int pow2[3], int B, int H, int N, hipStream_t stream);
+
+// Resident workgroup slots of `kernel` at `block_threads` threads on the
+// current device: compute units x workgroups per compute unit.  Queried once
+// per (device, kernel, block size) and cached; thread-safe.  0 on a HIP error.
+long device_slots(const void* kernel, int block_threads);
+
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id.  This maps
 // the hardware id to a logical id so that each XCD receives one contiguous
 // range of logical ids (neighbouring query blocks of the same heads share the

@@ -38,15 +38,21 @@ Readings where the pages are silent:
     own float32 arithmetic, so near a rounding boundary either neighbour is a
     valid code, and the tests check that against the float64 quotient this
     module returns (quotients());
-  - V is quantised per block the same way, without the Hadamard matrix;
+  - V is quantised per block without the Hadamard matrix, with a power-of-two
+    scale s = 2^ceil(log2(amax / 448)) (the E8M0 form, which the FP8 matrix
+    instruction applies exactly; E4M3 is a floating format, so V's own
+    rounding error does not change), so that the V scale never has to ride
+    in P's E4M3 mantissa (see below);
   - inside attention P is quantised too (both products run on FP8 matrix
-    cores), jointly with the V scale of its key's block: write s_v(j) =
-    2^E_j r_j with E_j = ceil(log2 s_v(j)), so 1/2 < r_j <= 1; P_j is stored as
-    E4M3(256 p_j r_j) and stands for E4M3(256 p_j r_j) / (256 r_j) (the power
-    of two 2^E_j is exact and travels separately); p = exp(S - m) relative to
-    the row maximum, so 256 p r <= 256 stays inside E4M3 range, and the factor
-    256 keeps small p away from the subnormals; the row sum l uses the
-    unquantised p.
+    cores), jointly with the V scale of its key's block relative to the
+    largest V scale of the head: write s_v(j) / max_blocks s_v = 2^E_j r_j with
+    E_j = ceil(log2 of that ratio), so 1/2 < r_j <= 1 (r = 1 in the block with
+    the largest scale); P_j is stored as E4M3(256 p_j r_j) and stands for
+    E4M3(256 p_j r_j) / (256 r_j) (the power of two 2^E_j is exact and travels
+    separately); p = exp(S - m) relative to the row maximum, so 256 p r <= 256
+    stays inside E4M3 range, the largest weight of the largest-scale block is
+    exact, and the factor 256 keeps small p away from the subnormals whatever
+    the other blocks' magnitudes; the row sum l uses the unquantised p.
 """
 from __future__ import annotations
 
@@ -103,11 +109,12 @@ def e4m3_encode(x) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def quotients(x, hadamard: bool, block: int = BLOCK):
+def quotients(x, hadamard: bool, block: int = BLOCK, pow2: bool = False):
     """The per-block quantisation quotients y / s of a [B, H, N, d] tensor, in
     float64, and the block maxima A = max |y_u| (y_u = x H with the +-1 matrix,
-    or x without the transform).  Returns (t [B,H,N,d], A [B,H,ceil(N/block)]);
-    t is 0 in an all-zero block."""
+    or x without the transform).  With ``pow2`` the scale is the power of two
+    s = 2^ceil(log2(amax / 448)) instead of amax / 448.  Returns (t [B,H,N,d],
+    A [B,H,ceil(N/block)]); t is 0 in an all-zero block."""
     x = np.asarray(x, dtype=np.float64)
     B, H, N, d = x.shape
     yu = x @ sylvester_hadamard(d) if hadamard else x          # y = yu / sqrt(d)
@@ -119,20 +126,36 @@ def quotients(x, hadamard: bool, block: int = BLOCK):
         a = np.abs(blk).max(axis=(2, 3))
         amax[:, :, j] = a
         with np.errstate(divide="ignore", invalid="ignore"):
-            tj = (E4M3_MAX * blk) / a[:, :, None, None]         # y / s = 448 y_u / A, one rounding
+            if pow2:                                            # y / s, s a power of two: exact division
+                y = blk / np.sqrt(float(d)) if hadamard else blk
+                tj = y / pow2_scale(a / (E4M3_MAX * (np.sqrt(float(d)) if hadamard else 1.0)))[:, :, None, None]
+            else:
+                tj = (E4M3_MAX * blk) / a[:, :, None, None]     # y / s = 448 y_u / A, one rounding
         t[:, :, j * block:(j + 1) * block, :] = np.where(a[:, :, None, None] > 0, tj, 0.0)
     return t, amax
 
 
-def quantize_blocks(x, hadamard: bool, block: int = BLOCK):
+def pow2_scale(s):
+    """2^ceil(log2 s) for positive s (1 where s is 0): the power-of-two block
+    scale, the E8M0 form of a scale that the FP8 matrix instruction applies
+    exactly."""
+    s = np.asarray(s, dtype=np.float64)
+    E, _ = pow2_split(np.where(s > 0, s, 1.0))
+    return np.where(s > 0, np.ldexp(1.0, E), 1.0)
+
+
+def quantize_blocks(x, hadamard: bool, block: int = BLOCK, pow2: bool = False):
     """Incoherent processing (optional) then per-block FP8 quantisation of a
     [B, H, N, d] tensor: code = E4M3(y / s), s = amax / 448 (1 for an all-zero
-    block).  Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)])."""
+    block), or with ``pow2`` s = 2^ceil(log2(amax / 448)).  Returns (codes
+    uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)])."""
     d = np.shape(x)[-1]
-    t, amax_u = quotients(x, hadamard, block)
+    t, amax_u = quotients(x, hadamard, block, pow2)
     norm = E4M3_MAX * np.sqrt(float(d)) if hadamard else E4M3_MAX   # s = amax_u / (448 sqrt(d))
-    scales = np.where(amax_u > 0, amax_u / norm, 1.0).astype(np.float32)
-    return e4m3_encode(t), scales
+    s = np.where(amax_u > 0, amax_u / norm, 1.0)
+    if pow2:
+        s = pow2_scale(s)
+    return e4m3_encode(t), s.astype(np.float32)
 
 
 def pow2_split(s):
@@ -156,7 +179,8 @@ def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p
                   block: int = BLOCK):
     """Attention on dequantised FP8 operands, with P itself quantised as
     E4M3(256 p r)/(256 r) when ``quantize_p`` (r: the mantissa part in (1/2, 1]
-    of the key's V-block scale, see pow2_split; l from the unquantised p).
+    of the key's V-block scale over the head's largest, see pow2_split; l from
+    the unquantised p).
     Returns (O, LSE) in float64."""
     q = dequantize_blocks(q8, qs, block)
     k = dequantize_blocks(k8, ks, block)
@@ -175,7 +199,7 @@ def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p
             p = np.exp(s - m)
             l = p.sum(axis=1, keepdims=True)
             if quantize_p:
-                r = np.repeat(pow2_split(vs64[b, h])[1], block)[:N][None, :]
+                r = np.repeat(pow2_split(vs64[b, h] / vs64[b, h].max())[1], block)[:N][None, :]
                 pq = e4m3_decode(e4m3_encode(256.0 * p * r)) / (256.0 * r)
             else:
                 pq = p

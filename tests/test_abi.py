@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
                                     "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_hadamard_fp8_quant",
-                                    "fa_lse_merge", "fa_status_string"]
+                                    "fa_lse_merge", "fa_qkv_fp8_quant", "fa_status_string"]
 
 
 @pytest.fixture(scope="module")
@@ -89,6 +89,7 @@ def _sig(lib):
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, P]
     lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
     lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    lib.fa_qkv_fp8_quant.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
@@ -129,6 +130,32 @@ def test_quant_validation(lib):
     assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 0, 128, 1, None) == -2
     assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 8, 128, 3, None) == -6
     assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE, FAKE3, 1, 1, 8, 128, 1, None) == -6
+    # one head of the input is addressed with 32-bit byte offsets: N d sizeof(x) < 2^32
+    assert lib.fa_hadamard_fp8_quant(FAKE, 0, FAKE2, FAKE3, 1, 1, 1 << 23, 128, 1, None) == -2   # fp32
+    assert lib.fa_hadamard_fp8_quant(FAKE, 0, FAKE2, FAKE3, 1, 1, 1 << 23, 128, 0, None) == -2
+    assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 1 << 24, 128, 1, None) == -2   # bf16
+    assert lib.fa_hadamard_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 1 << 25, 64, 0, None) == -2
+
+
+@pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
+def test_qkv_quant_validation(lib):
+    _sig(lib)
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(9)]
+    f = lambda ptrs, dt=1, B=1, H=1, N=8, d=128, flags=5: lib.fa_qkv_fp8_quant(
+        ptrs[0], ptrs[1], ptrs[2], dt, *ptrs[3:], B, H, N, d, flags, None)
+    assert f([NULL] + p[1:]) == -1
+    assert f(p[:8] + [NULL]) == -1
+    assert f(p, dt=2) == -3
+    assert f(p, flags=8) == -6 and f(p, flags=-1) == -6
+    assert f(p, d=64) == -4
+    assert f(p, N=0) == -2 and f(p, B=0) == -2
+    assert f(p, dt=0, N=1 << 23) == -2 and f(p, N=1 << 24) == -2      # 32-bit offsets per head
+    q = list(p)
+    q[4] = q[1]                                                       # k8 aliases k
+    assert f(q) == -6
+    q = list(p)
+    q[8] = q[6]                                                       # v_scale aliases q_scale
+    assert f(q) == -6
 
 
 def test_decode_workspace_bytes(lib):

@@ -1,16 +1,21 @@
 """GPU parity of the FP8 attention kernel.
 
-Kernel correctness: the GPU result on codes/scales produced by the GPU
-quantiser (bit-identical to the oracle's, see test_gpu_quant.py) is compared
-with float64 attention on the same dequantised operands -- once without P
-quantisation (bound: relative RMSE 3e-2, which covers P's E4M3 rounding) and
-once with the oracle's emulation of P's quantisation (tighter bound); LSE does
-not see P's rounding and must match to 1e-3 relative.
+Kernel correctness: the GPU result on the codes/scales that the GPU quantiser
+produced (themselves checked against the float64 definition in
+test_gpu_quant.py) is compared with float64 attention on the same dequantised
+operands -- once without P quantisation (bound p_error_bound: 3e-2 with the
+power-of-two V scales of the library's FP8 path, else the emulated E4M3
+rounding error of P plus a quarter) and once with the oracle's emulation of
+P's quantisation (1.5e-2; the kernel's running reference maximum differs from
+the exact row maximum, so individual roundings differ); LSE does not see P's
+rounding and must match to 1e-3 relative.
 
 Specification (the FP8 workload: 2 x 16 heads, 8192 tokens, causal, 0.1% of
 Q/K coordinates at +-20): relative RMSE of O against float64 attention on the
-bf16 source values, with and without the Hadamard transform, over sampled
-rows of several heads.
+bf16 source values over the whole tensor (every head and row), with and
+without the Hadamard transform.  At the same size the kernel is also checked
+against float64 attention on its own dequantised operands, over the whole
+tensor and row by row.
 """
 import numpy as np
 import pytest
@@ -29,32 +34,46 @@ def rel_rmse(x, ref):
     return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
 
 
-def fp8_run(q, k, v, causal, scale, hadamard):
+def p_error_bound(o_emu, o_ref):
+    """Bound on the kernel's relative RMSE against float64 attention on its own
+    operands: P is rounded to E4M3 (3 mantissa bits, relative error up to 2^-4,
+    RMS about 2^-4 / sqrt(3) = 0.036 when a weight's mantissa position is
+    random).  With power-of-two V scales the largest weight of a row is stored
+    exactly and the error stays well below 3e-2; with float V scales that are
+    not the head's largest, the scale ratio's mantissa rides in P and every
+    weight rounds.  So: 3e-2, or the oracle's emulation of the same rounding
+    (quantize_p) plus a quarter, whichever is larger."""
+    return max(3e-2, 1.25 * rel_rmse(o_emu, o_ref) + 2e-3)
+
+
+def fp8_run(q, k, v, causal, scale, hadamard, pow2_v=True):
+    """The library's FP8 path: one quantiser launch (Q and K with or without the
+    transform, V with a power-of-two block scale unless pow2_v is False, then
+    amax / 448 like Q and K), then the FP8 attention kernel."""
     qd, kd, vd = (t.to("cuda:0").contiguous() for t in (q, k, v))
-    q8, qs = fa.quant_fp8(qd, hadamard=hadamard)
-    k8, ks = fa.quant_fp8(kd, hadamard=hadamard)
-    v8, vs = fa.quant_fp8(vd, hadamard=False)
+    (q8, qs), (k8, ks), (v8, vs) = fa.quant_qkv_fp8(qd, kd, vd, hadamard_qk=hadamard, hadamard_v=False, pow2_v=pow2_v)
     o, lse = fa.attention_fp8(q8, k8, v8, qs, ks, vs, causal=causal, scale=scale)
     torch.cuda.synchronize()
     ops = tuple(x.cpu().numpy() for x in (q8, k8, v8, qs, ks, vs))
     return f64(o), f64(lse), ops
 
 
+@pytest.mark.parametrize("pow2_v", [True, False])
 @pytest.mark.parametrize("hadamard", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 100, 128, 300, 1000])
-def test_fp8_kernel_vs_dequantised_oracle(gpu, N, causal, hadamard):
+def test_fp8_kernel_vs_dequantised_oracle(gpu, N, causal, hadamard, pow2_v):
     w = custom(1, 2, N, 128, causal, "fp8", seed=N * 3 + 1, outlier_frac=0.001)
     q, k, v = make_qkv(w)
-    o, lse, (q8, k8, v8, qs, ks, vs) = fp8_run(q, k, v, causal, w.scale, hadamard)
+    o, lse, (q8, k8, v8, qs, ks, vs) = fp8_run(q, k, v, causal, w.scale, hadamard, pow2_v)
     o_ref, lse_ref = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, causal, quantize_p=False)
     o_emu, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, causal, quantize_p=True)
     e_ref, e_emu = rel_rmse(o, o_ref), rel_rmse(o, o_emu)
     e_lse = float((np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max())
-    log(f"  N={N} causal={causal} hadamard={hadamard}: rel RMSE vs fp64 {e_ref:.4f}, vs P-emulation {e_emu:.4f},"
-        f" LSE {e_lse:.2e}")
+    log(f"  N={N} causal={causal} hadamard={hadamard} pow2_v={pow2_v}: rel RMSE vs fp64 {e_ref:.4f}, vs P-emulation "
+        f"{e_emu:.4f}, emulated P error {rel_rmse(o_emu, o_ref):.4f}, LSE {e_lse:.2e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    assert e_ref <= 3e-2
+    assert e_ref <= p_error_bound(o_emu, o_ref)
     assert e_emu <= 1.5e-2
     assert e_lse <= 1e-3
 
@@ -77,7 +96,7 @@ def test_fp8_scores_jump_between_tiles(gpu, causal):
     e_lse = float((np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max())
     log(f"  causal={causal}: rel RMSE vs fp64 {e_ref:.4f}, vs P-emulation {e_emu:.4f}, LSE {e_lse:.2e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    assert e_ref <= 3e-2
+    assert e_ref <= p_error_bound(o_emu, o_ref)
     assert e_emu <= 1.5e-2
     assert e_lse <= 1e-3
 
@@ -96,7 +115,8 @@ def test_fp8_unusual_scales(gpu, scale):
     q, k, v = make_qkv(w)
     o, lse, (q8, k8, v8, qs, ks, vs) = fp8_run(q, k, v, True, scale, True)
     o_ref, lse_ref = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, scale, True, quantize_p=False)
-    assert rel_rmse(o, o_ref) <= 3e-2
+    o_emu, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, scale, True, quantize_p=True)
+    assert rel_rmse(o, o_ref) <= p_error_bound(o_emu, o_ref)
     assert float((np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()) <= 1e-3
 
 
@@ -126,20 +146,93 @@ def _spec_errors(w, heads, nrows, seed):
     return out
 
 
-def test_fp8_workload_spec_bound(gpu):
-    """Relative RMSE <= 6e-2 against float64 attention on the bf16 sources, both arms.
+def _row_rel(o, ref):
+    """Relative error of every row (query) of O: ||o_i - ref_i|| / ||ref_i||."""
+    return np.linalg.norm(o - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
 
-    Under this input model the bound sits at the error floor: the CPU emulation
-    attributes ~0.05 (plain) / ~0.06 (Hadamard) to Q/K quantisation alone, ~0.026
-    to V and ~0.01 to P.  A regression bound of 8e-2 is asserted; exceeding 6e-2
-    is reported as an expected failure with the measured values."""
+
+@pytest.fixture(scope="module")
+def fp8_8k():
+    """Both arms of the FP8 workload on the GPU, and the float64 references over
+    the whole tensor: attention on the bf16 sources (the specification's
+    reference) and attention on each arm's own dequantised codes."""
     w = WORKLOADS["fp8_causal_8k"]
-    errs = _spec_errors(w, [(0, 0), (0, 7), (1, 3), (1, 15)], 256, 41)
-    log(f"[fp8_causal_8k] rel RMSE vs fp64 on bf16 sources: no Hadamard {errs[False]:.4f}, Hadamard {errs[True]:.4f}")
-    assert errs[False] <= 8e-2 and errs[True] <= 8e-2
-    if errs[False] > 6e-2 or errs[True] > 6e-2:
-        pytest.xfail(f"relative RMSE plain {errs[False]:.4f}, Hadamard {errs[True]:.4f}: at the 6e-2 bound's error "
-                     "floor for this input model (Q/K quantisation alone ~0.05-0.06)")
+    q, k, v = make_qkv(w)
+    log(f"[{w.name}] float64 attention on the bf16 sources, {w.B * w.H} heads")
+    o_src, _ = oracle.attention(f64(q), f64(k), f64(v), w.scale, w.causal)
+    res = {"w": w, "src": o_src}
+    for had in (False, True):
+        log(f"[{w.name}] GPU arm hadamard={had}, and float64 attention on its dequantised codes")
+        o, lse, ops = fp8_run(q, k, v, w.causal, w.scale, had)
+        o_deq, lse_deq = oracle.attention_fp8(*ops, w.scale, w.causal, quantize_p=False)
+        res[had] = {"o": o, "lse": lse, "ops": ops, "deq": o_deq, "lse_deq": lse_deq}
+    return res
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_fp8_kernel_vs_dequantised_oracle_full_size(gpu, fp8_8k, hadamard):
+    """The kernel at 8192 tokens against float64 attention on its own codes and
+    scales: whole-tensor relative RMSE <= 3e-2 (P's E4M3 rounding), every row
+    within 0.1 relative (a defect confined to a few rows or one d-block fails),
+    LSE within 1e-3 of max(1, |LSE|)."""
+    r = fp8_8k[hadamard]
+    e = rel_rmse(r["o"], r["deq"])
+    rows = _row_rel(r["o"], r["deq"])
+    e_lse = float((np.abs(r["lse"] - r["lse_deq"]) / np.maximum(1.0, np.abs(r["lse_deq"]))).max())
+    log(f"  hadamard={hadamard}: whole-tensor rel RMSE {e:.4f}, worst row {rows.max():.4f} "
+        f"(99.9th pct {np.percentile(rows, 99.9):.4f}), LSE {e_lse:.2e}")
+    assert np.all(np.isfinite(r["o"])) and np.all(np.isfinite(r["lse"]))
+    assert e <= 3e-2
+    assert rows.max() <= 0.1
+    assert e_lse <= 1e-3
+
+
+def test_fp8_emulation_at_full_size_on_two_heads(gpu, fp8_8k):
+    """The oracle's emulation of P's quantisation on the GPU's own codes, two heads of
+    each arm: the kernel agrees with it to 1.5e-2 (the reference maxima differ, so
+    individual P roundings differ)."""
+    for had in (False, True):
+        q8, k8, v8, qs, ks, vs = fp8_8k[had]["ops"]
+        sl = lambda x: x[:1, :2]
+        o_emu, _ = oracle.attention_fp8(sl(q8), sl(k8), sl(v8), sl(qs), sl(ks), sl(vs), fp8_8k["w"].scale, True,
+                                        quantize_p=True)
+        e = rel_rmse(sl(fp8_8k[had]["o"]), o_emu)
+        e_src_emu = rel_rmse(o_emu, sl(fp8_8k["src"]))
+        e_src_gpu = rel_rmse(sl(fp8_8k[had]["o"]), sl(fp8_8k["src"]))
+        log(f"  hadamard={had}: GPU vs emulation {e:.4f}; on these two heads vs the sources: GPU {e_src_gpu:.4f}, "
+            f"emulation {e_src_emu:.4f}")
+        assert e <= 1.5e-2
+
+
+def test_fp8_workload_spec_bound(gpu, fp8_8k):
+    """Relative RMSE <= 6e-2 against float64 attention on the bf16 sources, whole
+    tensor, both arms.  The plain arm is asserted.  The Hadamard arm sits at the
+    error floor of this input model (its Q/K quantisation alone costs ~0.06 in the
+    CPU emulation): a regression bound of 8e-2 is asserted and exceeding 6e-2 is an
+    expected failure carrying the whole-tensor values."""
+    e_plain = rel_rmse(fp8_8k[False]["o"], fp8_8k["src"])
+    e_had = rel_rmse(fp8_8k[True]["o"], fp8_8k["src"])
+    e_plain_deq = rel_rmse(fp8_8k[False]["deq"], fp8_8k["src"])
+    e_had_deq = rel_rmse(fp8_8k[True]["deq"], fp8_8k["src"])
+    log(f"[fp8_causal_8k] whole-tensor rel RMSE vs fp64 on the bf16 sources: plain {e_plain:.4f} (operand "
+        f"quantisation alone {e_plain_deq:.4f}), Hadamard {e_had:.4f} (operands alone {e_had_deq:.4f})")
+    assert e_plain <= 6e-2
+    assert e_had <= 8e-2
+    if e_had > 6e-2:
+        pytest.xfail(f"whole-tensor relative RMSE of the Hadamard arm {e_had:.4f} > 6e-2 (plain {e_plain:.4f}); "
+                     f"its quantised operands alone give {e_had_deq:.4f} in float64")
+
+
+def test_fp8_incoherent_processing_at_8k(gpu, fp8_8k):
+    """The pages' claim (lower FP8 error with the Hadamard transform) on the 8k workload itself, whole tensor."""
+    e_plain = rel_rmse(fp8_8k[False]["o"], fp8_8k["src"])
+    e_had = rel_rmse(fp8_8k[True]["o"], fp8_8k["src"])
+    log(f"[fp8_causal_8k] whole tensor: Hadamard {e_had:.4f} vs no Hadamard {e_plain:.4f}")
+    assert e_had <= 8e-2
+    if not e_had < e_plain:
+        pytest.xfail(f"Hadamard arm {e_had:.4f} >= plain FP8 {e_plain:.4f} over the whole tensor at 8192 tokens: "
+                     "with +-20 outliers equal to the block maximum the plain arm quantises them exactly, and "
+                     "spreading them costs more than it saves at this length (reproduced by the CPU emulation)")
 
 
 def test_fp8_incoherent_processing_lowers_error_at_2k(gpu):
@@ -149,17 +242,6 @@ def test_fp8_incoherent_processing_lowers_error_at_2k(gpu):
     log(f"[{w.name}] rel RMSE: no Hadamard {errs[False]:.4f}, Hadamard {errs[True]:.4f}")
     assert errs[True] < errs[False]
     assert errs[True] <= 6e-2
-
-
-def test_fp8_incoherent_processing_at_8k(gpu):
-    """The pages' claim (lower FP8 error with the Hadamard transform) on the 8k workload itself."""
-    w = WORKLOADS["fp8_causal_8k"]
-    errs = _spec_errors(w, [(0, 0), (0, 7), (1, 3), (1, 15)], 256, 43)
-    log(f"[fp8_causal_8k] Hadamard {errs[True]:.4f} vs no Hadamard {errs[False]:.4f}")
-    if not errs[True] < errs[False]:
-        pytest.xfail(f"Hadamard arm {errs[True]:.4f} >= plain FP8 {errs[False]:.4f} at 8192 tokens: with +-20 "
-                     "outliers equal to the block maximum the plain arm quantises them exactly, and spreading them "
-                     "costs more than it saves at this length (reproduced by the CPU emulation)")
 
 
 def test_fp8_incoherent_processing_on_channel_outliers(gpu):
@@ -176,3 +258,24 @@ def test_fp8_incoherent_processing_on_channel_outliers(gpu):
     if errs[True] > 6e-2:
         pytest.xfail(f"Hadamard arm {errs[True]:.4f} > 6e-2 at 8192 tokens (plain FP8 {errs[False]:.4f}): the "
                      "error grows with the sequence length, as on the sparse-outlier workload")
+
+
+@pytest.mark.parametrize("std", [1.0, 1e-3])
+def test_fp8_zero_v_block_and_small_v(gpu, std):
+    """An all-zero V block gets the unit scale; every other block's P keeps its
+    precision (each block's scale is its own power of two in the matrix op)."""
+    w = custom(1, 2, 400, 128, True, "fp8", seed=92)
+    q, k, v = make_qkv(w)
+    v = (v.float() * std).to(torch.bfloat16)
+    v[:, :, 256:384] = 0.0
+    o, lse, (q8, k8, v8, qs, ks, vs) = fp8_run(q, k, v, True, w.scale, True, pow2_v=False)
+    assert np.all(vs[:, :, 2] == 1.0)
+    o_ref, lse_ref = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, True, quantize_p=False)
+    o_emu, _ = oracle.attention_fp8(q8, k8, v8, qs, ks, vs, w.scale, True, quantize_p=True)
+    e_ref, e_emu = rel_rmse(o, o_ref), rel_rmse(o, o_emu)
+    log(f"  std={std}: rel RMSE vs fp64 {e_ref:.4f}, vs P-emulation {e_emu:.4f}, emulated P error "
+        f"{rel_rmse(o_emu, o_ref):.4f}")
+    # the zero block (scale 1) is the head's largest here, so every weight rounds:
+    # bounded by E4M3's own rounding, whatever V's magnitude
+    assert e_ref <= min(5e-2, p_error_bound(o_emu, o_ref)) and e_emu <= 1.5e-2
+    assert float((np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()) <= 1e-3

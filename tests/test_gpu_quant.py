@@ -11,7 +11,7 @@ import io_aware_exact_16_amd as fa
 import oracle
 from io_aware_exact_16_amd.workloads import WORKLOADS, custom, make_qkv
 
-from gpu_helpers import check_fp8_codes, log
+from gpu_helpers import check_fp8_codes, f64, log
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,43 @@ def test_deterministic(gpu):
     b = _quant(q, True)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N", [1, 300, 1000])
+def test_qkv_in_one_launch_equals_three_calls(gpu, N, dtype):
+    w = custom(2, 3, N, 128, True, "fp8", seed=N + 5, outlier_frac=0.001)
+    q, k, v = (t.to(dtype).to("cuda:0").contiguous() for t in make_qkv(w))
+    for had_qk, had_v in ((True, False), (False, False), (True, True)):
+        fused = fa.quant_qkv_fp8(q, k, v, hadamard_qk=had_qk, hadamard_v=had_v, pow2_v=False)
+        sep = (fa.quant_fp8(q, had_qk), fa.quant_fp8(k, had_qk), fa.quant_fp8(v, had_v))
+        torch.cuda.synchronize()
+        for (x8, s), (y8, t) in zip(fused, sep):
+            assert torch.equal(x8, y8) and torch.equal(s, t)
+
+
+@pytest.mark.parametrize("hadamard_v", [False, True])
+@pytest.mark.parametrize("N", [1, 300, 1000, 8192])
+def test_pow2_v_scales(gpu, N, hadamard_v):
+    """V with power-of-two block scales: without the transform y / s = x 2^-E is
+    exact, so the codes equal the oracle's bit for bit; with it, within the
+    float32 margin.  Q and K in the same launch are unaffected."""
+    w = custom(2, 2, N, 128, True, "fp8", seed=N + 9, outlier_frac=0.001)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = (t.to("cuda:0").contiguous() for t in (q, k, v))
+    (q8, qs), (k8, ks), (v8, vs) = fa.quant_qkv_fp8(qd, kd, vd, hadamard_qk=True, hadamard_v=hadamard_v, pow2_v=True)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_blocks(f64(v), hadamard_v, pow2=True)
+    np.testing.assert_array_equal(vs.cpu().numpy(), rs)
+    if hadamard_v:
+        t, _ = oracle.quotients(f64(v), True, pow2=True)
+        eps = 8 * 2.0 ** -24 * np.abs(f64(v)).sum(axis=3, keepdims=True) * 1.01 / (
+            np.sqrt(128.0) * np.repeat(rs.astype(np.float64), 128, axis=2)[:, :, :N, None]) + 4 * 2.0 ** -24 * np.abs(t)
+        val = oracle.e4m3_decode(v8.cpu().numpy())
+        lo = oracle.e4m3_decode(oracle.e4m3_encode(t - eps))
+        hi = oracle.e4m3_decode(oracle.e4m3_encode(t + eps))
+        assert np.all((val >= lo) & (val <= hi))
+    else:
+        np.testing.assert_array_equal(v8.cpu().numpy(), rc)
+    for x8, s, x in ((q8, qs, q), (k8, ks, k)):
+        assert check_fp8_codes(x, x8.cpu().numpy(), s.cpu().numpy(), True) <= 1e-3 * x8.numel() + 1

@@ -477,6 +477,31 @@ def test_quantize_codes_are_exact_nearest_e4m3(hadamard):
                 assert codes[0, hh, 128 * j + t, i] == want, (hh, j, t, i)
 
 
+def test_quantize_pow2_scales():
+    # power-of-two block scales: amax / 448 <= s < 2 amax / 448, s = 1 for a zero
+    # block, and each code is the exact E4M3 rounding of x / s (exhaustive search
+    # over all finite codes on exact rationals, for sampled elements)
+    g = torch.Generator().manual_seed(17)
+    x = torch.randn(1, 2, 300, 128, generator=g).to(torch.bfloat16).double().numpy()
+    x[0, 1, 128:256] = 0.0
+    codes, scales = oracle.quantize_blocks(x, False, pow2=True)
+    r = np.random.default_rng(8)
+    for hh in range(2):
+        for j in range(3):
+            blk = x[0, hh, 128 * j:128 * (j + 1)]
+            amax = np.abs(blk).max()
+            sc = float(scales[0, hh, j])
+            if amax == 0:
+                assert sc == 1.0 and np.all(codes[0, hh, 128 * j:128 * (j + 1)] & 0x7F == 0)
+                continue
+            assert math.frexp(sc)[0] == 0.5                            # a power of two
+            assert amax / 448.0 <= sc < 2.0 * amax / 448.0
+            for _ in range(200):
+                t, i = int(r.integers(blk.shape[0])), int(r.integers(128))
+                want = _nearest_e4m3_exact(Fraction(float(blk[t, i])) / Fraction(sc))
+                assert codes[0, hh, 128 * j + t, i] == want
+
+
 def test_quantize_exact_tie_with_hadamard_goes_to_even():
     # x = 20 H[3] + 0.9375 H[70] (rows of the +-1 matrix) gives y_u = x H =
     # 128 (20 e_3 + 0.9375 e_70): A = 2560 and coordinate 70 scales to exactly
@@ -569,11 +594,19 @@ def test_attention_fp8_p_quant_error_bound():
     vmax = np.abs(oracle.dequantize_blocks(v8, vs)).max()
     assert np.abs(o_q - o_n).max() <= (2.0 ** -4 + 256 * 2.0 ** -17) * vmax
     assert np.abs(o_q - o_n).max() > 0
+    # in a head with a single V block r = 1: the largest weight of each row (p = 1)
+    # is stored exactly
+    o_q1, _ = oracle.attention_fp8(q8[:, :, :128], k8[:, :, :128], v8[:, :, :128], qs[:, :, :1], ks[:, :, :1],
+                                   vs[:, :, :1], 128 ** -0.5, False, quantize_p=True)
+    o_h, _ = oracle.attention_fp8(q8[:, :, :128], k8[:, :, :128], v8[:, :, :128], qs[:, :, :1], ks[:, :, :1],
+                                  vs[:, :, :1] * 0.7, 128 ** -0.5, False, quantize_p=True)
+    np.testing.assert_allclose(o_h, 0.7 * o_q1, rtol=1e-7, atol=1e-12)   # r depends on the ratio only (float32 scale)
 
 
 def test_attention_fp8_p_quant_folds_v_block_scales():
     # with unequal V-block scales, P is quantised as E4M3(256 p r)/(256 r) with r
-    # the block scale over the next power of two up: one row against a scalar loop
+    # the block scale over the head's largest, over the next power of two up: one
+    # row against a scalar loop
     shape = (1, 1, 256, 128)
     q, k, v = (rng.standard_normal(shape) for _ in range(3))
     v[:, :, 128:] *= 3.0                                   # second V block has a larger scale
@@ -587,8 +620,8 @@ def test_attention_fp8_p_quant_folds_v_block_scales():
     p = np.exp(srow - srow.max())
     num = np.zeros(128)
     for j in range(256):
-        sv = float(vs[0, 0, j // 128])
-        r = sv / 2.0 ** math.ceil(math.log2(sv))
+        ratio = float(vs[0, 0, j // 128]) / float(vs[0, 0].max())
+        r = ratio / 2.0 ** math.ceil(math.log2(ratio))
         pq = float(oracle.e4m3_decode(oracle.e4m3_encode(256.0 * p[j] * r))) / (256.0 * r)
         num += pq * vd[0, 0, j]
     np.testing.assert_allclose(o[0, 0, i], num / p.sum(), rtol=0, atol=1e-12)
