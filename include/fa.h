@@ -31,9 +31,10 @@
  *   Stream:   `stream` is a hipStream_t (NULL = the default stream).  Work is
  *             enqueued asynchronously on it; the call never synchronises.
  *             Results are valid once the caller has synchronised that stream.
- *   Memory:   the library allocates nothing and keeps no mutable global state;
- *             concurrent calls from several host threads are safe (fa_fwd_decode
- *             and fa_bwd take their scratch space from the caller).
+ *   Memory:   the library allocates nothing; concurrent calls from several host
+ *             threads are safe (fa_fwd_decode and fa_bwd take their scratch space
+ *             from the caller), except fa_fwd_decode_noalloc, whose static device
+ *             scratch is shared by all its calls on one GPU.
  *   Errors:   arguments are checked before any HIP call.  On a negative status
  *             nothing has been enqueued and the outputs are untouched, except
  *             FA_ERR_LAUNCH, which reports a failed kernel launch.  Device
@@ -65,8 +66,9 @@ enum fa_status {
   FA_ERR_DTYPE = -3,        /* unknown dtype code, or FA_FP8_E4M3 passed to fa_fwd */
   FA_ERR_UNSUPPORTED = -4,  /* head dimension not supported for this dtype/entry point */
   FA_ERR_LAUNCH = -5,       /* the kernel launch failed (hipGetLastError) */
-  FA_ERR_ARG = -6           /* non-finite scale, flag not 0/1, an output aliasing an input, or a
+  FA_ERR_ARG = -6,          /* non-finite scale, flag not 0/1, an output aliasing an input, or a
                                workspace smaller than required */
+  FA_ERR_SCRATCH = -7       /* fa_fwd_decode_noalloc: the sizes need more than its static scratch */
 };
 
 /*
@@ -186,6 +188,26 @@ size_t fa_fwd_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_decode_noalloc -- fa_fwd_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels, with the partial results in a
+ * library-owned static device array of 16 MiB (FA_DECODE_SCRATCH_BYTES) instead
+ * of a caller workspace.  Arguments, layout and results as fa_fwd_decode.
+ *   Sizes whose fa_fwd_decode_workspace_bytes exceeds FA_DECODE_SCRATCH_BYTES
+ *   return FA_ERR_SCRATCH before any HIP call.
+ *   The call allocates nothing (no hipMalloc, no allocating library routine);
+ *   each GPU holds its own copy of the array from the library's first use on
+ *   it until the process ends, and its address is looked up once per device.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (two streams, or two host threads) race and give wrong results;
+ *   serialise them on one stream.  The array needs no clearing: every call
+ *   writes every partial result it reads.
+ */
+#define FA_DECODE_SCRATCH_BYTES (16u * 1024u * 1024u)
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
 
 /*
  * fa_lse_merge -- combine P partial attentions of the same queries over

@@ -21,9 +21,10 @@ _lib = None
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
-                -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG"}
+                -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG", -7: "FA_ERR_SCRATCH"}
+FA_DECODE_SCRATCH_BYTES = 16 * 1024 * 1024
 EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_qkv_fp8_quant", "fa_fwd_decode_workspace_bytes",
-            "fa_fwd_decode",
+            "fa_fwd_decode", "fa_fwd_decode_noalloc",
             "fa_lse_merge", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string")
 BLOCK = 128   # tokens per FP8 scaling block
 
@@ -59,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.fa_fwd_decode.restype = I
+    lib.fa_fwd_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.fa_fwd_decode_noalloc.restype = I
     lib.fa_lse_merge.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
     lib.fa_lse_merge.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
@@ -196,6 +199,22 @@ def fa_fwd_decode(q, k, v, o, lse, scale: float, causal: bool, workspace) -> Non
     st = load().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                               int(bool(causal)), _ptr(workspace), nbytes, _stream(q))
     _check("fa_fwd_decode", st)
+
+
+def fa_fwd_decode_noalloc(q, k, v, o, lse, scale: float, causal: bool) -> None:
+    """fa_fwd_decode with the partial results in the library's static device scratch
+    (FA_DECODE_SCRATCH_BYTES per GPU): allocates nothing; calls that overlap on one GPU race."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _dev4("q", q, torch.bfloat16)
+    _dev4("k", k, torch.bfloat16, (B, H, Nk, d))
+    _dev4("v", v, torch.bfloat16, (B, H, Nk, d))
+    _dev4("o", o, torch.bfloat16, (B, H, Nq, d))
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, Nq)):
+        raise ValueError("fa_fwd_decode_noalloc: lse must be a contiguous float32 CUDA tensor [B,H,Nq]")
+    st = load().fa_fwd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                                      int(bool(causal)), _stream(q))
+    _check("fa_fwd_decode_noalloc", st)
 
 
 def fa_lse_merge(o_parts, lse_parts, o, lse) -> None:

@@ -20,10 +20,19 @@
 // its partial O_s (float32, normalised) and LSE_s (-inf when the chunk holds
 // no key the query sees) to the caller's workspace.  A second kernel merges
 // the S parts per query row with the identity above.
+#include <mutex>
+
 #include "attn_bf16_common.h"
 
 namespace fa {
 namespace {
+
+// Library-owned scratch of the entry point that allocates nothing
+// (fa_fwd_decode_noalloc): the partial results of the split-KV kernel.  Each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (decode_scratch below).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 using namespace bf16k;
 
@@ -225,6 +234,25 @@ hipError_t launch_attn_decode_bf16(const void* q, const void* k, const void* v, 
                               : launch_decode_d<128, false>(q, k, v, op, lp, BH, Nq, Nk, S, chunk, scale, stream);
   return causal ? launch_decode_d<64, true>(q, k, v, op, lp, BH, Nq, Nk, S, chunk, scale, stream)
                 : launch_decode_d<64, false>(q, k, v, op, lp, BH, Nq, Nk, S, chunk, scale, stream);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with this device current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_lse_merge(const float* op, const float* lp, void* o, bool bf16_out, float* lse, int P, long rows,

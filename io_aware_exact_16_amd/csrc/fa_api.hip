@@ -13,6 +13,7 @@
 namespace {
 
 constexpr long long kMaxGrid = 2147483647LL;
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_SCRATCH_BYTES, "the header states the scratch size");
 
 bool sizes_ok(int B, int H, int N, int d, int rows_per_block) {
   if (B < 1 || H < 1 || N < 1) return false;
@@ -137,9 +138,15 @@ size_t fa_fwd_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   return (size_t)S * B * H * Nq * (size_t)(d + 1) * sizeof(float);
 }
 
-int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
-                  int d, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode entry points; the workspace size they need
+// goes to *need.
+int decode_checks(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H, int Nq,
+                  int Nk, int d, float scale, int causal, size_t* need) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, H, Nq, d, 32) || !sizes_ok(B, H, Nk, d, 64)) return FA_ERR_SHAPE;
   if ((long long)Nk * d * 4 >= (1LL << 32) || (long long)Nq * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;
@@ -149,18 +156,52 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
   fa::decode_split(B, H, Nq, Nk, &S, &chunk);
   const long long units = (long long)S * B * H * ((Nq + 31) / 32);
   if (units > kMaxGrid || (long long)B * H * Nq > kMaxGrid) return FA_ERR_SHAPE;
-  const size_t need = (size_t)S * B * H * Nq * (size_t)(d + 1) * sizeof(float);
-  if (workspace_bytes < need) return FA_ERR_ARG;
   const void* ins[3] = {q, k, v};
   for (const void* p : ins)
-    if (p == o || p == (const void*)lse || p == (const void*)workspace) return FA_ERR_ARG;
-  if ((void*)lse == o || workspace == o || workspace == (void*)lse) return FA_ERR_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p == o || p == (const void*)lse) return FA_ERR_ARG;
+  if ((const void*)lse == o) return FA_ERR_ARG;
+  *need = (size_t)S * B * H * Nq * (size_t)(d + 1) * sizeof(float);
+  return FA_OK;
+}
+
+int decode_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, void* workspace, hipStream_t s) {
+  int S = 0, chunk = 0;
+  fa::decode_split(B, H, Nq, Nk, &S, &chunk);
   float* op = static_cast<float*>(workspace);
   float* lp = op + (size_t)S * B * H * Nq * d;
   hipError_t e = fa::launch_attn_decode_bf16(q, k, v, op, lp, B, H, Nq, Nk, d, scale, causal != 0, s);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
   return launch_status(fa::launch_lse_merge(op, lp, o, true, lse, S, (long)B * H * Nq, d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const int st = decode_checks(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, &need);
+  if (st != FA_OK) return st;
+  if (!workspace) return FA_ERR_NULL;
+  if (workspace_bytes < need) return FA_ERR_ARG;
+  const void* ins[3] = {q, k, v};
+  for (const void* p : ins)
+    if (p == (const void*)workspace) return FA_ERR_ARG;
+  if (workspace == o || workspace == (void*)lse) return FA_ERR_ARG;
+  return decode_launch(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, workspace, static_cast<hipStream_t>(stream));
+}
+
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                          int Nk, int d, float scale, int causal, void* stream) {
+  size_t need = 0;
+  const int st = decode_checks(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, &need);
+  if (st != FA_OK) return st;
+  if (need > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+  return decode_launch(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, ws, static_cast<hipStream_t>(stream));
 }
 
 int fa_lse_merge(const float* o_parts, const float* lse_parts, int P, int B, int H, int N, int d, void* o,
@@ -215,6 +256,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ARG:
       return "invalid argument: non-finite scale, flag not 0/1, an output aliasing an input, or a workspace too small";
+    case FA_ERR_SCRATCH: return "the sizes need more scratch than the library's static device array holds";
     default: return "unknown status";
   }
 }

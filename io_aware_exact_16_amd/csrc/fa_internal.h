@@ -22,6 +22,11 @@ void decode_split(int B, int H, int Nq, int Nk, int* S, int* chunk);
 hipError_t launch_attn_decode_bf16(const void* q, const void* k, const void* v, float* op, float* lp, int B, int H,
                                    int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
 
+// Size of the library-owned device scratch of fa_fwd_decode_noalloc, and its
+// address on the current device (looked up once per device, thread-safe).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Merge P parts [P, rows, d] / [P, rows] into o [rows, d] (bf16 or float32) and lse [rows].
 hipError_t launch_lse_merge(const float* op, const float* lp, void* o, bool bf16_out, float* lse, int P, long rows,
                             int d, hipStream_t stream);

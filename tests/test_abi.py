@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
-                                    "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_hadamard_fp8_quant",
+                                    "fa_fwd_decode_noalloc", "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_hadamard_fp8_quant",
                                     "fa_lse_merge", "fa_qkv_fp8_quant", "fa_status_string"]
 
 
@@ -46,11 +46,11 @@ def test_binding_names_match_header():
 def test_status_strings(lib):
     lib.fa_status_string.restype = ctypes.c_char_p
     seen = set()
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         s = lib.fa_status_string(code).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert lib.fa_status_string(42).decode() == "unknown status"
 
 
@@ -93,6 +93,7 @@ def _sig(lib):
     lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.fa_fwd_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_lse_merge.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -244,3 +245,23 @@ def test_bwd_validation(lib):
     q = list(p)
     q[9] = q[4]                                                 # workspace aliases lse
     assert call(ptrs=q) == -6
+
+
+@pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
+def test_decode_noalloc_validation(lib):
+    """The same checks as fa_fwd_decode, and sizes whose partial results exceed the
+    static scratch return FA_ERR_SCRATCH before any HIP call."""
+    _sig(lib)
+    f = lambda ptrs, B=1, H=1, Nq=1, Nk=1024, d=128, scale=0.1, causal=1: lib.fa_fwd_decode_noalloc(
+        *ptrs, B, H, Nq, Nk, d, scale, causal, None)
+    p = [FAKE, FAKE2, FAKE3, FAKE4, FAKE5]
+    assert f([NULL] + p[1:]) == -1
+    assert f(p, d=96) == -4
+    assert f(p, Nq=2000, Nk=1000) == -2                 # causal needs Nq <= Nk
+    assert f(p, scale=float("nan")) == -6
+    assert f(p[:3] + [FAKE] + p[4:]) == -6             # o aliases q
+    need = lib.fa_fwd_decode_workspace_bytes(4, 32, 64, 8192, 128)
+    assert need > 16 * 1024 * 1024
+    assert f(p, B=4, H=32, Nq=64, Nk=8192) == -7
+    lib.fa_status_string.restype = ctypes.c_char_p
+    assert b"scratch" in lib.fa_status_string(-7)
