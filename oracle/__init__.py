@@ -23,9 +23,11 @@ from .attention import attention
 from .merge import lse_merge, decode_positions
 from .backward import attention_bwd
 from .fp8 import (sylvester_hadamard, orthonormal_hadamard, e4m3_decode, e4m3_encode,
-                  quantize_blocks, quotients, pow2_split, pow2_scale, dequantize_blocks, attention_fp8, E4M3_MAX,
+                  quantize_blocks, quotients, pow2_split, pow2_scale, dequantize_blocks, quantize_mx, dequantize_mx,
+                  attention_fp8, E4M3_MAX,
                   BLOCK)
 
 __all__ = ["attention", "attention_bwd", "lse_merge", "decode_positions", "sylvester_hadamard", "orthonormal_hadamard", "e4m3_decode", "e4m3_encode",
-           "quantize_blocks", "quotients", "pow2_split", "pow2_scale", "dequantize_blocks", "attention_fp8", "E4M3_MAX",
+           "quantize_blocks", "quotients", "pow2_split", "pow2_scale", "dequantize_blocks", "quantize_mx",
+           "dequantize_mx", "attention_fp8", "E4M3_MAX",
            "BLOCK"]

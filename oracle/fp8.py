@@ -38,6 +38,12 @@ Readings where the pages are silent:
     own float32 arithmetic, so near a rounding boundary either neighbour is a
     valid code, and the tests check that against the float64 quotient this
     module returns (quotients());
+  - variants (beyond the pages' pair of arms): MX-style scales, one power of
+    two per 32 consecutive coordinates of a token (the OCP microscaling
+    layout; the exponent is ceil(log2(amax / 448)) so that nothing clips),
+    which the FP8 matrix instruction applies per lane; and the Hadamard transform of V with
+    its inverse applied to O, which the orthogonality of the matrix allows
+    (O = P V = (P V H) H^T);
   - V is quantised per block without the Hadamard matrix, with a power-of-two
     scale s = 2^ceil(log2(amax / 448)) (the E8M0 form, which the FP8 matrix
     instruction applies exactly; E4M3 is a floating format, so V's own
@@ -168,6 +174,35 @@ def pow2_split(s):
     return E, np.where(exact, 1.0, m)
 
 
+def quantize_mx(x, hadamard: bool, group: int = 32):
+    """MX-style quantisation of a [B, H, N, d] tensor along d, after the optional
+    Hadamard transform: every group of 32 consecutive coordinates of a token row
+    shares a power-of-two scale X = 2^ceil(log2(amax / 448)), so the group's
+    largest magnitude lands in (224, 448] and nothing is clipped (the OCP
+    microscaling rule 2^(floor(log2 amax) - 8) would leave amax / X in
+    [256, 512) and clip the top of that range to 448), stored as its E8M0 code
+    E + 127 with E clamped to [-127, 127]; code = E4M3(y / X).  An all-zero
+    group gets code 0 (2^-127) and zero elements.  Returns (codes uint8
+    [B,H,N,d], e8m0 uint8 [B,H,N,d/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    y = x @ orthonormal_hadamard(d) if hadamard else x
+    g = y.reshape(B, H, N, d // group, group)
+    amax = np.abs(g).max(axis=-1)
+    E, _ = pow2_split(np.where(amax > 0, amax / E4M3_MAX, 1.0))      # ceil(log2(amax / 448))
+    E = np.clip(np.where(amax > 0, E, -127), -127, 127)
+    t = g / np.ldexp(1.0, E)[..., None]                                # exact: a power of two
+    codes = e4m3_encode(np.clip(t, -E4M3_MAX, E4M3_MAX)).reshape(B, H, N, d)
+    return codes, (E + 127).astype(np.uint8)
+
+
+def dequantize_mx(codes, e8m0, group: int = 32) -> np.ndarray:
+    """code * 2^(e8m0 - 127) over groups of 32 along the last axis, in float64."""
+    vals = e4m3_decode(codes)
+    sc = np.ldexp(1.0, np.asarray(e8m0, dtype=np.int64) - 127)
+    return vals * np.repeat(sc, group, axis=-1)
+
+
 def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
     """code * (float32 scale of its block), in float64."""
     vals = e4m3_decode(codes)
@@ -176,15 +211,23 @@ def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
 
 
 def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p: bool = True,
-                  block: int = BLOCK):
+                  block: int = BLOCK, q_mx=None, k_mx=None, v_hadamard: bool = False):
     """Attention on dequantised FP8 operands, with P itself quantised as
     E4M3(256 p r)/(256 r) when ``quantize_p`` (r: the mantissa part in (1/2, 1]
     of the key's V-block scale over the head's largest, see pow2_split; l from
-    the unquantised p).
-    Returns (O, LSE) in float64."""
+    the unquantised p).  ``q_mx`` / ``k_mx``: E8M0 codes [B,H,N,d/32] of MX
+    scales that multiply Q's / K's elements on top of their block scales.
+    ``v_hadamard``: V's codes hold V H / sqrt(d) (the Hadamard transform of V);
+    the output is transformed back, O = (P V') H / sqrt(d) (the orthonormal
+    Sylvester matrix is symmetric and its own inverse).  Returns (O, LSE) in
+    float64."""
     q = dequantize_blocks(q8, qs, block)
     k = dequantize_blocks(k8, ks, block)
     v = dequantize_blocks(v8, vs, block)
+    if q_mx is not None:
+        q = q * np.repeat(np.ldexp(1.0, np.asarray(q_mx, dtype=np.int64) - 127), 32, axis=-1)
+    if k_mx is not None:
+        k = k * np.repeat(np.ldexp(1.0, np.asarray(k_mx, dtype=np.int64) - 127), 32, axis=-1)
     B, H, N, d = q.shape
     idx = np.arange(N)
     o = np.empty((B, H, N, v.shape[3]))
@@ -205,4 +248,6 @@ def attention_fp8(q8, k8, v8, qs, ks, vs, scale: float, causal: bool, quantize_p
                 pq = p
             o[b, h] = (pq @ v[b, h]) / l
             lse[b, h] = (m + np.log(l))[:, 0]
+    if v_hadamard:
+        o = o @ orthonormal_hadamard(v.shape[3])
     return o, lse

@@ -502,6 +502,57 @@ def test_quantize_pow2_scales():
                 assert codes[0, hh, 128 * j + t, i] == want
 
 
+def test_quantize_mx_exact():
+    # MX-style groups of 32 coordinates: X = 2^E with E the smallest integer such
+    # that amax <= 448 2^E (found here by exact comparison), and every code the
+    # exact E4M3 rounding of x / X (exhaustive search on exact rationals)
+    g = torch.Generator().manual_seed(19)
+    x = torch.randn(1, 2, 40, 128, generator=g)
+    x[0, 0, 3, 5] = 20.0                                         # an outlier widens one group only
+    x[0, 1, 7, :32] = 0.0                                        # an all-zero group
+    x = x.to(torch.bfloat16).double().numpy()
+    codes, e8 = oracle.quantize_mx(x, False)
+    assert e8.shape == (1, 2, 40, 4) and e8.dtype == np.uint8
+    assert e8[0, 1, 7, 0] == 0 and np.all(codes[0, 1, 7, :32] == 0)
+    r = np.random.default_rng(9)
+    for _ in range(600):
+        hh, t, i = int(r.integers(2)), int(r.integers(40)), int(r.integers(128))
+        grp = x[0, hh, t, 32 * (i // 32):32 * (i // 32) + 32]
+        amax = Fraction(float(np.abs(grp).max()))
+        if amax == 0:
+            continue
+        E = -200
+        while amax > 448 * Fraction(2) ** E:
+            E += 1
+        assert int(e8[0, hh, t, i // 32]) == E + 127
+        assert codes[0, hh, t, i] == _nearest_e4m3_exact(Fraction(float(x[0, hh, t, i])) / Fraction(2) ** E)
+    deq = oracle.dequantize_mx(codes, e8)
+    assert np.all(np.abs(deq - x) <= np.abs(x) * 2.0 ** -4 + 2.0 ** -10 * np.repeat(
+        np.ldexp(1.0, e8.astype(np.int64) - 127), 32, axis=-1) + 1e-300)
+
+
+def test_attention_fp8_variants_compose_pinned_parts():
+    # MX scales on Q and K multiply their elements; V's Hadamard variant holds the
+    # codes of V H / sqrt(d) and transforms the output back: with exact operands
+    # both equal plain attention on the dequantised values
+    shape = (1, 2, 150, 128)
+    q, k, v = (rng.standard_normal(shape) for _ in range(3))
+    q8, qe = oracle.quantize_mx(q, True)
+    k8, ke = oracle.quantize_mx(k, True)
+    vh8, vhs = oracle.quantize_blocks(v, True)                   # codes of V H / sqrt(d)
+    ones = np.ones((1, 2, 2), dtype=np.float32)
+    o, lse = oracle.attention_fp8(q8, k8, vh8, ones, ones, vhs, 0.09, True, quantize_p=False, q_mx=qe, k_mx=ke,
+                                  v_hadamard=True)
+    qd, kd = oracle.dequantize_mx(q8, qe), oracle.dequantize_mx(k8, ke)
+    vd = oracle.dequantize_blocks(vh8, vhs) @ oracle.orthonormal_hadamard(128)    # back to V's coordinates
+    o_ref, lse_ref = attention(qd, kd, vd, 0.09, True)
+    np.testing.assert_allclose(o, o_ref, atol=1e-11)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-11)
+    # and both are close to attention on the unquantised inputs (FP8 rounding only)
+    o_src, _ = attention(q, k, v, 0.09, True)
+    assert np.linalg.norm(o - o_src) / np.linalg.norm(o_src) < 0.06
+
+
 def test_quantize_exact_tie_with_hadamard_goes_to_even():
     # x = 20 H[3] + 0.9375 H[70] (rows of the +-1 matrix) gives y_u = x H =
     # 128 (20 e_3 + 0.9375 e_70): A = 2560 and coordinate 70 scales to exactly
