@@ -87,23 +87,52 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
- * fa_fwd_fp8 -- fused attention forward on per-block-scaled E4M3 operands.
- *   q8, k8, v8        : [B,H,N,128] E4M3 bytes (typically from fa_hadamard_fp8_quant,
+ * fa_fwd_fp8 -- fused attention forward on per-block-scaled E4M3 operands
+ * ("FlashAttention-3 (PT)", section "Inovacoes tecnicas", item 3: low-precision
+ * FP8 matrix products, with Q and K made incoherent by an orthogonal
+ * transform; section "Novos recursos de hardware": FP8 doubles the matrix
+ * throughput).
+ *   q8, k8, v8        : [B,H,N,128] E4M3 bytes (typically from fa_qkv_fp8_quant,
  *                       with the Hadamard matrix applied to q and k and not to v).
  *   q_scale, k_scale,
  *   v_scale           : [B,H,ceil(N/128)] float32 block scales; element value = code * scale.
  *   o                 : [B,H,N,128] bfloat16 output;  lse : [B,H,N] float32 output.
  *   d                 : must be 128.
  * S = scale * (q8 k8^T) runs on FP8 matrix cores with the two block scales
- * folded into the softmax exponent; P is quantised to E4M3 as 256*p (p <= 1),
- * multiplied with v8 on FP8 matrix cores, and the v scale and 1/256 are undone
- * in float32.  (The dtype argument of fa_fwd has no room for the block scales,
- * hence a separate entry point.)
+ * folded into the softmax exponent.  P is quantised to E4M3 as 256 p r, where
+ * r in (1/2, 1] is the mantissa of the key block's V scale over the head's
+ * largest, whose power of two goes into the matrix instruction's E8M0 scale of
+ * the V operand (r = 1 everywhere when the V scales are powers of two, as
+ * fa_qkv_fp8_quant's FA_QUANT_POW2_SCALE_V makes them); 1/256 and the largest
+ * V scale are undone in float32.  (The dtype argument of fa_fwd has no room for
+ * the block scales, hence a separate entry point.)
  */
 int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                const float* q_scale, const float* k_scale, const float* v_scale,
                void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Flags of fa_fwd_fp8_ex. */
+enum fa_fp8_flags {
+  FA_FP8_V_HADAMARD = 1   /* v8 holds the codes of V H / sqrt(128) (fa_qkv_fp8_quant with
+                             FA_QUANT_HADAMARD_V); the output is transformed back, O = O' H / sqrt(128) */
+};
+
+/*
+ * fa_fwd_fp8_ex -- fa_fwd_fp8 with two variants of the FP8 path (same passage):
+ *   q_mx, k_mx : NULL, or both [B,H,N,4] E8M0 codes (fa_mx_fp8_quant): one
+ *                power-of-two scale 2^(code - 127) per 32 coordinates of each
+ *                token, multiplying q8 / k8 on top of their block scales (pass
+ *                block scales of 1 for pure MX operands); the matrix
+ *                instruction applies them per lane in S = Q K^T.  One of the two
+ *                NULL: FA_ERR_ARG.
+ *   flags      : 0 or FA_FP8_V_HADAMARD (other bits: FA_ERR_ARG).
+ * Everything else as fa_fwd_fp8, which equals fa_fwd_fp8_ex(..., NULL, NULL, ..., 0).
+ */
+int fa_fwd_fp8_ex(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                  const float* q_scale, const float* k_scale, const float* v_scale,
+                  const uint8_t* q_mx, const uint8_t* k_mx, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal, int flags, void* stream);
 
 /*
  * fa_hadamard_fp8_quant -- incoherent processing and per-block FP8 quantisation
@@ -126,6 +155,26 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  */
 int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scales,
                           int B, int H, int N, int d, int hadamard, void* stream);
+
+/*
+ * fa_mx_fp8_quant -- MX-style FP8 quantisation (a variant of incoherent
+ * processing's quantisation step, same passage as fa_hadamard_fp8_quant): every
+ * group of 32 consecutive coordinates of a token row shares one power-of-two
+ * scale X = 2^E, E = ceil(log2(amax / 448)) clamped to [-127, 127], so the
+ * group's largest magnitude lands in (224, 448] and nothing clips; code =
+ * E4M3 round-to-nearest-even of y / X.
+ *   x        : [B,H,N,128] input, in_dtype FA_BF16 or FA_F32.
+ *   x8       : [B,H,N,128] E4M3 output bytes.
+ *   e8m0     : [B,H,N,4] output, E + 127 per group (0 for an all-zero group,
+ *              whose codes are zero); the layout fa_fwd_fp8_ex reads.
+ *   hadamard : 1 = first the normalised Hadamard transform, as in
+ *              fa_hadamard_fp8_quant (then E and the quotient are formed in
+ *              float32 from the float32 transform: codes within that error of a
+ *              rounding boundary may go to either neighbour); 0 = none, and
+ *              y / X is exact.
+ */
+int fa_mx_fp8_quant(const void* x, int in_dtype, uint8_t* x8, uint8_t* e8m0, int B, int H, int N, int d,
+                    int hadamard, void* stream);
 
 /* Flags of fa_qkv_fp8_quant. */
 enum fa_quant_flags {

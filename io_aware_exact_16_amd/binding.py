@@ -23,7 +23,7 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
                 -4: "FA_ERR_UNSUPPORTED", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_ARG", -7: "FA_ERR_SCRATCH"}
 FA_DECODE_SCRATCH_BYTES = 16 * 1024 * 1024
-EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_hadamard_fp8_quant", "fa_qkv_fp8_quant", "fa_fwd_decode_workspace_bytes",
+EXPORTED = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_ex", "fa_hadamard_fp8_quant", "fa_mx_fp8_quant", "fa_qkv_fp8_quant", "fa_fwd_decode_workspace_bytes",
             "fa_fwd_decode", "fa_fwd_decode_noalloc",
             "fa_lse_merge", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_string")
 BLOCK = 128   # tokens per FP8 scaling block
@@ -54,6 +54,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = I
     lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
     lib.fa_hadamard_fp8_quant.restype = I
+    lib.fa_mx_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    lib.fa_mx_fp8_quant.restype = I
+    lib.fa_fwd_fp8_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P]
+    lib.fa_fwd_fp8_ex.restype = I
     lib.fa_qkv_fp8_quant.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.fa_qkv_fp8_quant.restype = I
     lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -132,6 +136,47 @@ def fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, scale: float, caus
     st = load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o),
                            _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), _stream(q8))
     _check("fa_fwd_fp8", st)
+
+
+FA_FP8_V_HADAMARD = 1
+
+
+def fa_fwd_fp8_ex(q8, k8, v8, q_scale, k_scale, v_scale, q_mx, k_mx, o, lse, scale: float, causal: bool,
+                  flags: int) -> None:
+    """fa_fwd_fp8 with MX-style E8M0 scales for Q and K (uint8 [B,H,N,4], both or neither
+    None) and ``flags`` (FA_FP8_V_HADAMARD: v8 holds the codes of V H / sqrt(128))."""
+    B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _dev4(name, t, torch.uint8, (B, H, N, d))
+    _dev4("o", o, torch.bfloat16, (B, H, N, d))
+    nb = -(-N // BLOCK)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and tuple(t.shape) == (B, H, nb)):
+            raise ValueError(f"fa_fwd_fp8_ex: {name} must be a contiguous float32 CUDA tensor [B,H,{nb}]")
+    for name, t in (("q_mx", q_mx), ("k_mx", k_mx)):
+        if t is not None:
+            _dev4(name, t, torch.uint8, (B, H, N, d // 32))
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
+        raise ValueError("fa_fwd_fp8_ex: lse must be a contiguous float32 CUDA tensor [B,H,N]")
+    st = load().fa_fwd_fp8_ex(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(q_mx),
+                              _ptr(k_mx), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), int(flags),
+                              _stream(q8))
+    _check("fa_fwd_fp8_ex", st)
+
+
+def fa_mx_fp8_quant(x, x8, e8m0, hadamard: bool) -> None:
+    """x8 (uint8 E4M3) and e8m0 (uint8 [B,H,N,4]) <- MX-style quantisation of x (bf16 or
+    fp32, [B,H,N,128]): one power-of-two scale per 32 coordinates of a row, after the
+    normalised Hadamard transform when ``hadamard``."""
+    code = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(x.dtype)
+    if code is None:
+        raise ValueError(f"fa_mx_fp8_quant: unsupported dtype {x.dtype}")
+    B, H, N, d = x.shape
+    _dev4("x", x, x.dtype)
+    _dev4("x8", x8, torch.uint8, (B, H, N, d))
+    _dev4("e8m0", e8m0, torch.uint8, (B, H, N, d // 32))
+    st = load().fa_mx_fp8_quant(_ptr(x), code, _ptr(x8), _ptr(e8m0), B, H, N, d, int(bool(hadamard)), _stream(x))
+    _check("fa_mx_fp8_quant", st)
 
 
 def fa_hadamard_fp8_quant(x, x8, scales, hadamard: bool) -> None:
@@ -299,6 +344,27 @@ def attention_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, s
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
     fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, scale, causal)
+    return o, lse
+
+
+def quant_mx_fp8(x, hadamard: bool = True):
+    """Return (x8, e8m0) from fa_mx_fp8_quant."""
+    B, H, N, d = x.shape
+    x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    e8 = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=x.device)
+    fa_mx_fp8_quant(x, x8, e8, hadamard)
+    return x8, e8
+
+
+def attention_fp8_ex(q8, k8, v8, q_scale, k_scale, v_scale, q_mx=None, k_mx=None, causal: bool = False,
+                     scale: float | None = None, v_hadamard: bool = False):
+    """Return (o bf16, lse fp32) from fa_fwd_fp8_ex."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q8.shape[-1])
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8_ex(q8, k8, v8, q_scale, k_scale, v_scale, q_mx, k_mx, o, lse, scale, causal,
+                  FA_FP8_V_HADAMARD if v_hadamard else 0)
     return o, lse
 
 

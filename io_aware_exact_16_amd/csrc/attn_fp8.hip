@@ -26,7 +26,9 @@
 //    inside E4M3 range (448), and the O rescale is rare.
 //  * Layouts as in the bf16 kernel (S^T and O^T accumulators; per-lane
 //    softmax state).  32x32x64 FP8 MFMA operands: lane l holds row (col)
-//    l % 32 and the 32 consecutive k values 32 * (l / 32) + 0..31.  V^T comes
+//    l % 32; its bytes 0..15 are k = 16 (l / 32) + 0..15 and bytes 16..31 are
+//    k = 32 + 16 (l / 32) + 0..15 (measured through the E8M0 block scales, whose
+//    32-element blocks are k = 0..31 and 32..63).  V^T comes
 //    from the row-major LDS tile through ds_read_b64_tr_b8: within each
 //    16-lane group, lane 2r + c names the 8 bytes at [r][8c..8c+7] of an
 //    8 x 16 byte tile and lane j receives column j (verified on gfx950).
@@ -79,6 +81,60 @@ __device__ __forceinline__ f32x16 mfma_fp8_scaled_a(const i32x8& a, const i32x8&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
 }
 
+// S-product variant with both operands scaled per lane (MX-style E8M0 scales
+// of the 32 coordinates each lane holds, in byte 0 of sa / sb).
+__device__ __forceinline__ f32x16 mfma_fp8_scaled_ab(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa,
+                                                     uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4, voffset + soffset, 0, 0, 0);
+}
+
+// O = O' H / sqrt(d) for the Hadamard variant of V (the normalised Sylvester
+// matrix is symmetric and its own inverse), on this lane's half of one
+// query's output: register r = 4a + e of acc[db] holds coordinate
+// 32 db + 8 a + 4 half + e, so six of the seven butterfly stages are in
+// registers and the stage over coordinate bit 2 pairs lane l with l ^ 32.
+// The 1 / sqrt(d) is left to the caller.
+__device__ __forceinline__ void fwht_o(f32x16 (&acc)[4], int half) {
+#pragma unroll
+  for (int bit = 1; bit < 16; bit <<= 1) {   // e bits (coordinate bits 0, 1), a bits (3, 4)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!(r & bit)) {
+          const float x = acc[db][r], y = acc[db][r | bit];
+          acc[db][r] = x + y;
+          acc[db][r | bit] = x - y;
+        }
+  }
+#pragma unroll
+  for (int bit = 1; bit < 4; bit <<= 1)      // db bits (coordinate bits 5, 6)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      if (!(db & bit)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = acc[db][r], y = acc[db | bit][r];
+          acc[db][r] = x + y;
+          acc[db | bit][r] = x - y;
+        }
+      }
+  const float sgn = half ? -1.0f : 1.0f;     // coordinate bit 2: half 0 keeps x + y, half 1 keeps x - y
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t u = __float_as_uint(acc[db][r]);
+      const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      // p[0]: the lower half-wave's value of this column, p[1]: the upper one's
+      acc[db][r] = __builtin_fmaf(__uint_as_float(p[1]), sgn, __uint_as_float(p[0]));
+    }
+}
+
 // Constants of one 128-key block: c_t = softmax constant with the Q and K
 // block scales folded in; lr = log2(256 r); inv_r = 1 / (256 r); ve = E8M0
 // code of 2^E, where s_v / max s_v = 2^E r, 1/2 < r <= 1.  A ratio below
@@ -128,12 +184,19 @@ constexpr float P_SLACK = 0.8f;   // log2 of the allowed growth of p above 1
 constexpr int VMCNT(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
 // One 64-key tile of one wave, with the constants of its 128-key block.
-template <bool CAUSAL, bool MASK>
+template <bool CAUSAL, bool MASK, bool MX>
 __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const uint32_t (&koff)[2][2],
                                           const uint32_t (&voff)[4], const i32x8 (&qf)[2], f32x16 (&acc)[4],
                                           float& m2, float& lsum, const BlockK& bk, int j0, int qi, int N,
-                                          int half) {
+                                          int half, const uint32_t* kmx, int arow, uint32_t qsc) {
   const float c_t = bk.c_t;
+  // MX: the E8M0 scales of this lane's K row (4 per key, one per 32 coordinates),
+  // shifted so that byte 2 dc holds the group of d-chunk dc this lane reads
+  uint32_t kw[2] = {0u, 0u};
+  if (MX) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) kw[kb] = kmx[arow + 32 * kb] >> (8 * half);
+  }
   constexpr int KB_BYTES = 32 * D;   // one 32-key block of the tile
   constexpr int KG_BYTES = 16 * D;   // 16 keys
   f32x16 s[2];
@@ -148,7 +211,10 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
       const uint4 a0 = *reinterpret_cast<const uint4*>(kt + koff[dc][0] + kb * KB_BYTES);
       const uint4 a1 = *reinterpret_cast<const uint4*>(kt + koff[dc][1] + kb * KB_BYTES);
       const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      s[kb] = mfma_fp8(a, qf[dc], s[kb]);
+      if (MX)
+        s[kb] = mfma_fp8_scaled_ab(a, qf[dc], s[kb], kw[kb] >> (16 * dc), qsc >> (16 * dc));
+      else
+        s[kb] = mfma_fp8(a, qf[dc], s[kb]);
     }
 
   if (MASK) {
@@ -215,7 +281,7 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
   }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool MX, bool VHAD>
 // Three waves per SIMD for causal attention: this kernel is bound by its
 // softmax VALU work, and a third resident wave fills more of the VALU's idle
 // cycles (the causal build fits 168 VGPRs, spilling one value used only at
@@ -224,11 +290,13 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c0, uint32_t qflip) {
+    const uint8_t* __restrict__ QMX, const uint8_t* __restrict__ KMX, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, int N, int nqb, int total, float c0, uint32_t qflip) {
   constexpr int TILE_CHUNKS = BC * D / 16;   // 16-byte chunks per K (or V) tile
   constexpr int NW = NT / 64;
   constexpr int LPW = TILE_CHUNKS / NT;      // DMA instructions per wave, tensor and tile
   __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
+  __shared__ uint32_t kmxs[MX ? 2 : 1][MX ? BC : 1];   // MX: the K tile's E8M0 scales, 4 per key
 
   const int L = xcd_logical_id(blockIdx.x, total);
   const int bh = L / nqb;
@@ -251,26 +319,41 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
   for (int off = 32; off > 0; off >>= 1) svmax = fmaxf(svmax, __shfl_xor(svmax, off));
   const float c_q = c0 * QS[(size_t)bh * nsb + q0 / QBLK];
 
-  // Q^T as the B operand: lane holds query qi, bytes 64*dc + 32*half + 0..31
+  // Q^T as the B operand: lane holds query qi and two 16-byte chunks of d-chunk
+  // dc.  The matrix instruction takes bytes 0..15 of half-wave h as k = 16 h +
+  // 0..15 and bytes 16..31 as k = 32 + 16 h + 0..15; any placement shared by Q
+  // and K gives the same product, and the MX variant needs k = d - 64 dc, so
+  // that each 32-element scale block is one group of 32 coordinates.  Without
+  // MX the lane holds d = 64 dc + 32 half + 0..31, with MX
+  // d = 64 dc + 16 half + 0..15 and 64 dc + 32 + 16 half + 0..15.
   i32x8 qf[2];
 #pragma unroll
   for (int dc = 0; dc < 2; ++dc) {
     uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
     if (qi < N) {
-      const uint4* src = reinterpret_cast<const uint4*>(Q8 + hoff + (size_t)qi * D + 64 * dc + 32 * half);
-      u0 = src[0];
-      u1 = src[1];
+      const uint8_t* row = Q8 + hoff + (size_t)qi * D + 64 * dc;
+      u0 = *reinterpret_cast<const uint4*>(row + (MX ? 16 * half : 32 * half));
+      u1 = *reinterpret_cast<const uint4*>(row + (MX ? 32 + 16 * half : 32 * half + 16));
     }
     qf[dc] = i32x8{(int)(u0.x ^ qflip), (int)(u0.y ^ qflip), (int)(u0.z ^ qflip), (int)(u0.w ^ qflip),
                    (int)(u1.x ^ qflip), (int)(u1.y ^ qflip), (int)(u1.z ^ qflip), (int)(u1.w ^ qflip)};
   }
+
+  // MX: this query's four E8M0 scales, shifted so that byte 2 dc holds the group of d-chunk dc
+  uint32_t qsc = 0;
+  if (MX) {
+    const uint32_t qmx = qi < N ? *reinterpret_cast<const uint32_t*>(QMX + ((size_t)bh * N + qi) * 4) : 0x7F7F7F7Fu;
+    qsc = qmx >> (8 * half);
+  }
+  const int arow = key_of_arow(l32);
 
   // this lane's LDS byte offsets: K operand rows (two 16-byte chunks per d-half) ...
   uint32_t koff[2][2];
 #pragma unroll
   for (int dc = 0; dc < 2; ++dc)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) koff[dc][i] = 16 * lds_chunk8(key_of_arow(l32), 4 * dc + 2 * half + i);
+    for (int i = 0; i < 2; ++i)   // the same 16-byte chunks of the key row as Q's (see above)
+      koff[dc][i] = 16 * lds_chunk8(key_of_arow(l32), MX ? 4 * dc + 2 * i + half : 4 * dc + 2 * half + i);
   // ... and 8-bit transposed V reads (keys 8*(G/2) + r of the first group, d-block db)
   uint32_t voff[4];
   {
@@ -293,6 +376,8 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     const int sw = (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
     lane_off[i] = (uint32_t)(row * D + 16 * (slot ^ sw));
   }
+  const __amdgpu_buffer_rsrc_t kmxrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? KMX + (size_t)bh * N * 4 : K8), 0, (uint32_t)N * 4, 0x00020000);
   auto issue_tile = [&](int j0, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     const uint32_t base = (uint32_t)j0 * D;
@@ -302,6 +387,7 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
       lds_dma16(krs, &smem[BUF][0][slot0], lane_off[i], base);
       lds_dma16(vrs, &smem[BUF][1][slot0], lane_off[i], base);
     }
+    if (MX && wave == 0) lds_dma4(kmxrs, &kmxs[MX ? BUF : 0][0], 4 * lane, (uint32_t)j0 * 4);   // 64 keys x 4 B
   };
 
   f32x16 acc[4];
@@ -320,10 +406,11 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     if (CAUSAL && j0 > qw + 31) return;
     const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
     const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
+    const uint32_t* km = &kmxs[MX ? BUF : 0][0];
     if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
-      tile_math<CAUSAL, true>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half);
+      tile_math<CAUSAL, true, MX>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half, km, arow, qsc);
     else
-      tile_math<CAUSAL, false>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half);
+      tile_math<CAUSAL, false, MX>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half, km, arow, qsc);
   };
 
   issue_tile(0, IC<0>{});
@@ -333,10 +420,12 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     if (t + 1 < ntiles) step(t + 1, bk, IC<1>{});
   }
 
-  // epilogue: O = acc max s_v / (256 l), LSE = ln 2 * (m2 + log2 l)
+  // epilogue: O = acc max s_v / (256 l) (then H / sqrt(d) for the Hadamard
+  // variant of V), LSE = ln 2 * (m2 + log2 l)
   const float ltot = wave_halves_sum(lsum);
+  if (VHAD) fwht_o(acc, half);               // every lane, before the row guard: the stage pairs lanes
   if (qi < N) {
-    const float f = svmax / (256.0f * ltot);
+    const float f = svmax / (256.0f * ltot) * (VHAD ? 0.08838834764831845f : 1.0f);   // 1 / sqrt(128)
     uint16_t* orow = O + hoff + (size_t)qi * D;
     typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 #pragma unroll
@@ -352,25 +441,37 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
   }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool MX, bool VHAD>
 hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* qs, const float* ks,
-                  const float* vs, void* o, float* lse, int B, int H, int N, float scale, hipStream_t stream) {
+                  const float* vs, const uint8_t* qmx, const uint8_t* kmx, void* o, float* lse, int B, int H, int N,
+                  float scale, hipStream_t stream) {
   const int nqb = (N + BR - 1) / BR;
   const int total = nqb * H * B;
   const float c0 = (float)((double)__builtin_fabsf(scale) * 1.4426950408889634);
   const uint32_t qflip = scale < 0.0f ? 0x80808080u : 0u;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(NT), 0, stream, q8, k8, v8, qs, ks, vs,
-                     static_cast<uint16_t*>(o), lse, N, nqb, total, c0, qflip);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, MX, VHAD>), dim3(total), dim3(NT), 0, stream, q8, k8, v8, qs, ks,
+                     vs, qmx, kmx, static_cast<uint16_t*>(o), lse, N, nqb, total, c0, qflip);
   return hipGetLastError();
+}
+
+template <bool CAUSAL>
+hipError_t launch_c(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* qs, const float* ks,
+                    const float* vs, const uint8_t* qmx, const uint8_t* kmx, bool vhad, void* o, float* lse, int B,
+                    int H, int N, float scale, hipStream_t stream) {
+  const bool mx = qmx != nullptr;
+  if (mx) return vhad ? launch<CAUSAL, true, true>(q8, k8, v8, qs, ks, vs, qmx, kmx, o, lse, B, H, N, scale, stream)
+                      : launch<CAUSAL, true, false>(q8, k8, v8, qs, ks, vs, qmx, kmx, o, lse, B, H, N, scale, stream);
+  return vhad ? launch<CAUSAL, false, true>(q8, k8, v8, qs, ks, vs, qmx, kmx, o, lse, B, H, N, scale, stream)
+              : launch<CAUSAL, false, false>(q8, k8, v8, qs, ks, vs, qmx, kmx, o, lse, B, H, N, scale, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* qs, const float* ks,
-                           const float* vs, void* o, float* lse, int B, int H, int N, float scale, bool causal,
-                           hipStream_t stream) {
-  return causal ? launch<true>(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, scale, stream)
-                : launch<false>(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, scale, stream);
+                           const float* vs, const uint8_t* qmx, const uint8_t* kmx, bool v_hadamard, void* o,
+                           float* lse, int B, int H, int N, float scale, bool causal, hipStream_t stream) {
+  return causal ? launch_c<true>(q8, k8, v8, qs, ks, vs, qmx, kmx, v_hadamard, o, lse, B, H, N, scale, stream)
+                : launch_c<false>(q8, k8, v8, qs, ks, vs, qmx, kmx, v_hadamard, o, lse, B, H, N, scale, stream);
 }
 
 }  // namespace fa

@@ -73,20 +73,30 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                                            scale, causal, s));
 }
 
-int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
-               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H, int N, int d,
-               float scale, int causal, void* stream) {
+int fa_fwd_fp8_ex(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                  const float* k_scale, const float* v_scale, const uint8_t* q_mx, const uint8_t* k_mx, void* o,
+                  float* lse, int B, int H, int N, int d, float scale, int causal, int flags, void* stream) {
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, H, N, d, 64)) return FA_ERR_SHAPE;
   if ((long long)N * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;   // same per-head limit as fa_fwd
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
-  const void* ins[6] = {q8, k8, v8, q_scale, k_scale, v_scale};
+  if ((q_mx == nullptr) != (k_mx == nullptr)) return FA_ERR_ARG;   // MX scales for both Q and K, or neither
+  if (flags & ~FA_FP8_V_HADAMARD) return FA_ERR_ARG;
+  const void* ins[8] = {q8, k8, v8, q_scale, k_scale, v_scale, q_mx, k_mx};
   for (const void* p : ins)
-    if (p == o || p == (const void*)lse) return FA_ERR_ARG;
+    if (p && (p == o || p == (const void*)lse)) return FA_ERR_ARG;
   if ((void*)lse == o) return FA_ERR_ARG;
-  return launch_status(fa::launch_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, scale, causal,
+  return launch_status(fa::launch_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, q_mx, k_mx,
+                                           (flags & FA_FP8_V_HADAMARD) != 0, o, lse, B, H, N, scale, causal,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  return fa_fwd_fp8_ex(q8, k8, v8, q_scale, k_scale, v_scale, nullptr, nullptr, o, lse, B, H, N, d, scale, causal,
+                       0, stream);
 }
 
 int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scales, int B, int H, int N, int d,
@@ -101,6 +111,19 @@ int fa_hadamard_fp8_quant(const void* x, int in_dtype, uint8_t* x8, float* scale
   if ((const void*)x8 == x || (const void*)scales == x || (void*)scales == (void*)x8) return FA_ERR_ARG;
   return launch_status(fa::launch_hadamard_fp8_quant(x, in_dtype == FA_BF16, x8, scales, B, H, N, d, hadamard != 0,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+int fa_mx_fp8_quant(const void* x, int in_dtype, uint8_t* x8, uint8_t* e8m0, int B, int H, int N, int d,
+                    int hadamard, void* stream) {
+  if (!x || !x8 || !e8m0) return FA_ERR_NULL;
+  if (in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_DTYPE;
+  if (hadamard != 0 && hadamard != 1) return FA_ERR_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, H, N, d, 128)) return FA_ERR_SHAPE;
+  if ((long long)N * d * (in_dtype == FA_F32 ? 4 : 2) >= (1LL << 32)) return FA_ERR_SHAPE;
+  if ((const void*)x8 == x || (const void*)e8m0 == x || (void*)e8m0 == (void*)x8) return FA_ERR_ARG;
+  return launch_status(fa::launch_mx_fp8_quant(x, in_dtype == FA_BF16, x8, e8m0, B, H, N, hadamard != 0,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int fa_qkv_fp8_quant(const void* q, const void* k, const void* v, int in_dtype, uint8_t* q8, uint8_t* k8,

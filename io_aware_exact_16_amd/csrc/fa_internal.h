@@ -42,12 +42,19 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int B, int H, int N, int d, float scale, bool causal, hipStream_t stream);
 
+// qmx / kmx: both null, or MX-style E8M0 scales [B*H, N, 4]; v_hadamard: V's
+// codes hold V H / sqrt(d) and O is transformed back in the epilogue.
 hipError_t launch_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
-                           const float* qs, const float* ks, const float* vs, void* o, float* lse,
+                           const float* qs, const float* ks, const float* vs, const uint8_t* qmx,
+                           const uint8_t* kmx, bool v_hadamard, void* o, float* lse,
                            int B, int H, int N, float scale, bool causal, hipStream_t stream);
 
 hipError_t launch_hadamard_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8, float* scales,
                                      int B, int H, int N, int d, bool hadamard, hipStream_t stream);
+
+// MX-style quantisation (d = 128): one E8M0 scale per 32 coordinates of a row.
+hipError_t launch_mx_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8, uint8_t* e8m0, int B, int H, int N,
+                               bool hadamard, hipStream_t stream);
 
 // Q, K and V (d = 128, one shape) in one launch, each with its own transform
 // and power-of-two-scale flags.

@@ -50,8 +50,22 @@ struct QuantJobs {
   float* s[3];
   int had[3];
   int pow2[3];   // power-of-two scale 2^ceil(log2(amax / 448)) instead of amax / 448
+  uint8_t* mx[3];   // non-null: MX mode, one E8M0 scale per 32 coordinates of a row ([N, d / 32] per head)
   int njobs;
 };
+
+// 2^-E and the E8M0 code E + 127 of the power-of-two scale 2^E, E =
+// ceil(log2(amax / denom)) clamped to [-127, 127], for amax > 0; the
+// multiplier that forms y / 2^E from the unnormalised transform y_u also
+// carries 1 / sqrt(d) (rnorm).
+__device__ __forceinline__ float pow2_multiplier(float amax, double denom, double rnorm, int* e8) {
+  int e;
+  const double m = frexp((double)amax / denom, &e);
+  int E = m == 0.5 ? e - 1 : e;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  *e8 = E + 127;
+  return (float)(ldexp(1.0, -E) * rnorm);
+}
 
 template <int D, bool BF16IN>
 __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const QuantJobs jobs, int N, int nb,
@@ -99,12 +113,16 @@ __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const QuantJo
   uint8_t* held_dst = nullptr;
   float held_scale = 0.0f;
   float* held_sdst = nullptr;
+  uint8_t* held_mx = nullptr;                // MX mode: this thread's two E8M0 codes
+  uint32_t held_mxv = 0;
   auto flush = [&]() {
     if (held_dst) {
 #pragma unroll
       for (int i = 0; i < EPT / 16; ++i) *reinterpret_cast<uint4*>(held_dst + 16 * i) = held[i];
     }
     if (held_sdst) *held_sdst = held_scale;
+    if (held_mx) *reinterpret_cast<uint16_t*>(held_mx) = (uint16_t)held_mxv;
+    held_mx = nullptr;
   };
 
   // one block: its tile is in cur (its DMA is complete after the wait below),
@@ -160,6 +178,34 @@ __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const QuantJo
           x[i] = __builtin_fmaf(x[i], sgn, other);
         }
       }
+    }
+
+    uint8_t* const MXO = jo == 0 ? jobs.mx[0] : (jo == 1 ? jobs.mx[1] : jobs.mx[2]);
+    if (MXO) {   // MX mode: this thread's 64 values are two whole groups of 32
+      const double rnorm = had ? 1.0 / __builtin_sqrt((double)D) : 1.0;
+      uint32_t e8pair = 0;
+#pragma unroll
+      for (int gi = 0; gi < EPT / 32; ++gi) {
+        float ga = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ga = fmaxf(ga, fabsf(x[32 * gi + i]));
+        int e8 = 0;
+        const float mul = ga > 0.0f ? pow2_multiplier(ga, had ? denom_had : 448.0, rnorm, &e8) : 0.0f;
+        e8pair |= (uint32_t)e8 << (8 * gi);
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+          const int e = 32 * gi + i;
+          uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(x[e] * mul, x[e + 1] * mul, 0, false);
+          const uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(x[e + 2] * mul, x[e + 3] * mul, p, true);
+          reinterpret_cast<uint32_t*>(held)[(32 * gi + i) / 4] = wv;
+        }
+      }
+      uint8_t* const X8 = jo == 0 ? jobs.x8[0] : (jo == 1 ? jobs.x8[1] : jobs.x8[2]);
+      held_dst = r0 + row < N ? X8 + (size_t)bh * N * D + (size_t)(r0 + row) * D + part * EPT : nullptr;
+      held_mx = r0 + row < N ? MXO + ((size_t)bh * N + r0 + row) * (D / 32) + part * (EPT / 32) : nullptr;
+      held_mxv = e8pair;
+      held_sdst = nullptr;
+      return;
     }
 
     float amax = 0.0f;
@@ -338,6 +384,17 @@ hipError_t launch_hadamard_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8,
                      : launch_plain<128, false>(x, x8, scales, B, H, N, stream);
   return x_is_bf16 ? launch_plain<64, true>(x, x8, scales, B, H, N, stream)
                    : launch_plain<64, false>(x, x8, scales, B, H, N, stream);
+}
+
+hipError_t launch_mx_fp8_quant(const void* x, bool x_is_bf16, uint8_t* x8, uint8_t* e8m0, int B, int H, int N,
+                               bool hadamard, hipStream_t stream) {
+  QuantJobs jobs = {};
+  jobs.x[0] = x;
+  jobs.x8[0] = x8;
+  jobs.mx[0] = e8m0;
+  jobs.had[0] = hadamard ? 1 : 0;
+  jobs.njobs = 1;
+  return x_is_bf16 ? launch<128, true>(jobs, B, H, N, stream) : launch<128, false>(jobs, B, H, N, stream);
 }
 
 hipError_t launch_qkv_fp8_quant(const void* const x[3], bool x_is_bf16, uint8_t* const x8[3], float* const scales[3],

@@ -21,8 +21,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode",
-                                    "fa_fwd_decode_noalloc", "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8", "fa_hadamard_fp8_quant",
-                                    "fa_lse_merge", "fa_qkv_fp8_quant", "fa_status_string"]
+                                    "fa_fwd_decode_noalloc", "fa_fwd_decode_workspace_bytes", "fa_fwd_fp8",
+                                    "fa_fwd_fp8_ex", "fa_hadamard_fp8_quant", "fa_lse_merge", "fa_mx_fp8_quant",
+                                    "fa_qkv_fp8_quant", "fa_status_string"]
 
 
 @pytest.fixture(scope="module")
@@ -90,6 +91,8 @@ def _sig(lib):
     lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
     lib.fa_hadamard_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
     lib.fa_qkv_fp8_quant.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.fa_mx_fp8_quant.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    lib.fa_fwd_fp8_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P]
     lib.fa_fwd_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
@@ -265,3 +268,24 @@ def test_decode_noalloc_validation(lib):
     assert f(p, B=4, H=32, Nq=64, Nk=8192) == -7
     lib.fa_status_string.restype = ctypes.c_char_p
     assert b"scratch" in lib.fa_status_string(-7)
+
+
+@pytest.mark.skipif(gpu_available(), reason="fake-pointer validation runs only where no GPU is visible")
+def test_fp8_variant_validation(lib):
+    _sig(lib)
+    assert lib.fa_mx_fp8_quant(NULL, 1, FAKE2, FAKE3, 1, 1, 8, 128, 1, None) == -1
+    assert lib.fa_mx_fp8_quant(FAKE, 2, FAKE2, FAKE3, 1, 1, 8, 128, 1, None) == -3
+    assert lib.fa_mx_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 8, 64, 0, None) == -4
+    assert lib.fa_mx_fp8_quant(FAKE, 1, FAKE2, FAKE3, 1, 1, 8, 128, 2, None) == -6
+    assert lib.fa_mx_fp8_quant(FAKE, 1, FAKE, FAKE3, 1, 1, 8, 128, 1, None) == -6
+    assert lib.fa_mx_fp8_quant(FAKE, 0, FAKE2, FAKE3, 1, 1, 1 << 23, 128, 1, None) == -2
+    p = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
+    f = lambda ptrs, d=128, flags=0: lib.fa_fwd_fp8_ex(*ptrs, 1, 1, 8, d, 0.1, 1, flags, None)
+    assert f(p[:6] + [NULL] + p[7:]) == -6                           # q_mx without k_mx
+    assert f(p[:7] + [NULL] + p[8:]) == -6                           # k_mx without q_mx
+    assert f(p, flags=2) == -6
+    assert f(p, d=64) == -4
+    q = list(p)
+    q[8] = q[6]                                                       # o aliases q_mx
+    assert f(q) == -6
+    assert f([NULL] + p[1:]) == -1
