@@ -55,7 +55,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   constexpr int TILE_CHUNKS = BC * CPR;      // chunks per K (or V) tile
   constexpr int NW = NT / 64;
   constexpr int LPW = TILE_CHUNKS / NT;      // DMA instructions per wave, tensor and tile
-  __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
+  // Separate objects for the two K and V buffers, so the compiler never orders
+  // a read of one buffer behind the DMA into the other (with one array it
+  // waited for the next tile's DMA before every P V product).
+  __shared__ uint4 kb0[TILE_CHUNKS], kb1[TILE_CHUNKS], vb0[TILE_CHUNKS], vb1[TILE_CHUNKS];
 
   const int L = xcd_logical_id(blockIdx.x, total);
   const int bh = L / nqb;
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int slot0 = (i * NW + wave) * 64;
-      lds_dma16(krs, &smem[BUF][0][slot0], lane_off[i], base);
-      lds_dma16(vrs, &smem[BUF][1][slot0], lane_off[i], base);
+      lds_dma16(krs, (BUF ? kb1 : kb0) + slot0, lane_off[i], base);
+      lds_dma16(vrs, (BUF ? vb1 : vb0) + slot0, lane_off[i], base);
     }
   };
 
@@ -136,8 +139,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     __syncthreads();                         // ... and every other wave's; the other buffer is free
     if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
     if (CAUSAL && j0 > qw + 31) return;      // the whole tile is above this wave's diagonal
-    const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
-    const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
+    const char* kt = reinterpret_cast<const char*>(BUF ? kb1 : kb0);
+    const char* vt = reinterpret_cast<const char*>(BUF ? vb1 : vb0);
     if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
       tile_math<D, CAUSAL, true>(kt, vt, koff, voff, qf, acc, m2, lsum, c, j0, qi, N, half);
     else
