@@ -72,7 +72,10 @@ enum fa_status {
 };
 
 /*
- * fa_fwd -- fused attention forward in float32 or bfloat16.
+ * fa_fwd -- fused attention forward in float32 or bfloat16: O = softmax(scale
+ * Q K^T + mask) V and its LSE, tile by tile with the online softmax, the score
+ * matrix never in HBM ("Flash Attention" glossary page, second paragraph;
+ * "FlashAttention-3 (PT)", section "FlashAttention e FlashAttention-2").
  *   q, k, v : [B,H,N,d] inputs, dtype `dtype` (FA_F32 or FA_BF16).
  *   o       : [B,H,N,d] output, same dtype as the inputs.
  *   lse     : [B,H,N] float32 output, natural-log units of the scaled scores.

@@ -63,5 +63,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-only AddressSanitizer + UndefinedBehaviorSanitizer build of the C entry
+# points (argument checks and dispatch), linked with the regular kernel objects:
+# _build/libfa_hostasan.so.  Every sanitizer flag is scoped to the host pass.
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+ASAN_LIB = os.path.join(BUILD, "libfa_hostasan.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that a process loading the host-ASan library must preload."""
+    r = subprocess.run([hipcc().replace("hipcc", "amdclang++"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return path
+
+
+def build_asan() -> str:
+    build()                                              # the regular objects the entry points link against
+    obj = os.path.join(BUILD, "fa_api_hostasan.o")
+    cmd = [hipcc(), *COMMON_FLAGS, "-g", *HOST_SAN, "-c", os.path.join(CSRC, "fa_api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("host-ASan compile of fa_api.hip failed:\n" + r.stderr)
+    objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "fa_api.hip"]
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-shared-libasan", *HOST_SAN, "-o", ASAN_LIB, obj,
+           *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link of the host-ASan library failed:\n" + r.stderr)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

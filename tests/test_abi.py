@@ -10,7 +10,8 @@ import pytest
 from conftest import ROOT, gpu_available
 
 HEADER = os.path.join(ROOT, "include", "fa.h")
-LIB = os.path.join(ROOT, "io_aware_exact_16_amd", "libfa.so")
+# FA_ABI_LIB: another build of the same library to check (the host-sanitizer build)
+LIB = os.environ.get("FA_ABI_LIB") or os.path.join(ROOT, "io_aware_exact_16_amd", "libfa.so")
 
 
 def declared_functions():
