@@ -6,6 +6,10 @@
 // leaves Q K^T unchanged) with the same tiling / online softmax as the bf16
 // kernel ("Flash Attention" glossary page, second paragraph).
 //
+// Persistent: one workgroup (4 waves, 128 query rows per work item) per
+// resident slot, three slots per compute unit for causal attention, walking a
+// static balanced list of (head, query block) items grouped per XCD.
+//
 // Inputs are E4M3 codes with one float32 scale per (b, h, 128-token block).
 //  * S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales)
 //    over the codes; the two block scales fold into the softmax constant of
@@ -291,60 +295,37 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     const uint8_t* __restrict__ QMX, const uint8_t* __restrict__ KMX, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, int N, int nqb, int total, float c0, uint32_t qflip) {
+    float* __restrict__ LSE, int N, int nqb, int BH, int groups, float c0, uint32_t qflip) {
   constexpr int TILE_CHUNKS = BC * D / 16;   // 16-byte chunks per K (or V) tile
   constexpr int NW = NT / 64;
   constexpr int LPW = TILE_CHUNKS / NT;      // DMA instructions per wave, tensor and tile
   __shared__ uint4 smem[2][2][TILE_CHUNKS];  // [buffer][K | V][chunk]
   __shared__ uint32_t kmxs[MX ? 2 : 1][MX ? BC : 1];   // MX: the K tile's E8M0 scales, 4 per key
 
-  const int L = xcd_logical_id(blockIdx.x, total);
-  const int bh = L / nqb;
-  int qb = L - bh * nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;             // longest query blocks first
-  const int q0 = qb * BR;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Persistent: workgroup g walks a static list of work items (head, block of
+  // 128 query rows).  Heads are split into `groups` sets (8 when the heads
+  // divide evenly: workgroup g runs on XCD g % 8, so the workgroups of an XCD
+  // stream the same heads' K/V through its L2); within a set the items go head
+  // by head, each head's blocks longest first, dealt to the set's workgroups in
+  // snake order (s, S - 1 - s, s, ...), which balances the causal work.  Every
+  // slot stays occupied until the list runs out (a grid of one workgroup per
+  // item left a third of the slots idle in launch gaps and the tail).
+  const int G = gridDim.x, g = blockIdx.x;
+  const int xg = g % groups, sl = g / groups, S = G / groups;
+  const int hx = BH / groups, nloc = hx * nqb;
+  auto item = [&](int r, int& bh_, int& qb_) -> bool {
+    const int k = r * S + ((r & 1) ? S - 1 - sl : sl);
+    if (k >= nloc) return false;
+    const int hl = k / nqb;
+    bh_ = xg * hx + hl;
+    qb_ = k - hl * nqb;
+    if (CAUSAL) qb_ = nqb - 1 - qb_;         // longest query blocks first
+    return true;
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int qw = q0 + 32 * wave;
-  const int qi = qw + l32;
-  const size_t hoff = (size_t)bh * N * D;
   const int nsb = (N + QBLK - 1) / QBLK;     // scaling blocks per head
-  const float* vsh = VS + (size_t)bh * nsb;
-  const float* ksh = KS + (size_t)bh * nsb;
-
-  // largest V-block scale of the head (every lane of the wave ends with it)
-  float svmax = 0.0f;
-  for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, vsh[i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) svmax = fmaxf(svmax, __shfl_xor(svmax, off));
-  const float c_q = c0 * QS[(size_t)bh * nsb + q0 / QBLK];
-
-  // Q^T as the B operand: lane holds query qi and two 16-byte chunks of d-chunk
-  // dc.  The matrix instruction takes bytes 0..15 of half-wave h as k = 16 h +
-  // 0..15 and bytes 16..31 as k = 32 + 16 h + 0..15; any placement shared by Q
-  // and K gives the same product, and the MX variant needs k = d - 64 dc, so
-  // that each 32-element scale block is one group of 32 coordinates.  Without
-  // MX the lane holds d = 64 dc + 32 half + 0..31, with MX
-  // d = 64 dc + 16 half + 0..15 and 64 dc + 32 + 16 half + 0..15.
-  i32x8 qf[2];
-#pragma unroll
-  for (int dc = 0; dc < 2; ++dc) {
-    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-    if (qi < N) {
-      const uint8_t* row = Q8 + hoff + (size_t)qi * D + 64 * dc;
-      u0 = *reinterpret_cast<const uint4*>(row + (MX ? 16 * half : 32 * half));
-      u1 = *reinterpret_cast<const uint4*>(row + (MX ? 32 + 16 * half : 32 * half + 16));
-    }
-    qf[dc] = i32x8{(int)(u0.x ^ qflip), (int)(u0.y ^ qflip), (int)(u0.z ^ qflip), (int)(u0.w ^ qflip),
-                   (int)(u1.x ^ qflip), (int)(u1.y ^ qflip), (int)(u1.z ^ qflip), (int)(u1.w ^ qflip)};
-  }
-
-  // MX: this query's four E8M0 scales, shifted so that byte 2 dc holds the group of d-chunk dc
-  uint32_t qsc = 0;
-  if (MX) {
-    const uint32_t qmx = qi < N ? *reinterpret_cast<const uint32_t*>(QMX + ((size_t)bh * N + qi) * 4) : 0x7F7F7F7Fu;
-    qsc = qmx >> (8 * half);
-  }
   const int arow = key_of_arow(l32);
 
   // this lane's LDS byte offsets: K operand rows (two 16-byte chunks per d-half) ...
@@ -352,23 +333,16 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int dc = 0; dc < 2; ++dc)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)   // the same 16-byte chunks of the key row as Q's (see above)
+    for (int i = 0; i < 2; ++i)   // the same 16-byte chunks of the key row as Q's (see below)
       koff[dc][i] = 16 * lds_chunk8(key_of_arow(l32), MX ? 4 * dc + 2 * i + half : 4 * dc + 2 * half + i);
   // ... and 8-bit transposed V reads (keys 8*(G/2) + r of the first group, d-block db)
   uint32_t voff[4];
   {
-    const int G = lane >> 4, j = lane & 15, r = j >> 1, cc = j & 1;
-    const int key = 8 * (G >> 1) + r;
+    const int GG = lane >> 4, j = lane & 15, r = j >> 1, cc = j & 1;
+    const int key = 8 * (GG >> 1) + r;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) voff[db] = 16 * lds_chunk8(key, 2 * db + (G & 1)) + 8 * cc;
+    for (int db = 0; db < 4; ++db) voff[db] = 16 * lds_chunk8(key, 2 * db + (GG & 1)) + 8 * cc;
   }
-
-  const int kend = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
-
-  const uint32_t nbytes = (uint32_t)N * D;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K8 + hoff), 0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V8 + hoff), 0, nbytes, 0x00020000);
   uint32_t lane_off[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
@@ -376,68 +350,120 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
     const int sw = (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
     lane_off[i] = (uint32_t)(row * D + 16 * (slot ^ sw));
   }
-  const __amdgpu_buffer_rsrc_t kmxrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? KMX + (size_t)bh * N * 4 : K8), 0, (uint32_t)N * 4, 0x00020000);
-  auto issue_tile = [&](int j0, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const uint32_t base = (uint32_t)j0 * D;
+
+  for (int r = 0;; ++r) {
+    int bh, qb;
+    if (!item(r, bh, qb)) break;
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int qi = qw + l32;
+    const size_t hoff = (size_t)bh * N * D;
+    const float* vsh = VS + (size_t)bh * nsb;
+    const float* ksh = KS + (size_t)bh * nsb;
+
+    // largest V-block scale of the head (every lane of the wave ends with it)
+    float svmax = 0.0f;
+    for (int i = lane; i < nsb; i += 64) svmax = fmaxf(svmax, vsh[i]);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int slot0 = (i * NW + wave) * 64;
-      lds_dma16(krs, &smem[BUF][0][slot0], lane_off[i], base);
-      lds_dma16(vrs, &smem[BUF][1][slot0], lane_off[i], base);
+    for (int off = 32; off > 0; off >>= 1) svmax = fmaxf(svmax, __shfl_xor(svmax, off));
+    const float c_q = c0 * QS[(size_t)bh * nsb + q0 / QBLK];
+
+    // Q^T as the B operand: lane holds query qi and two 16-byte chunks of d-chunk
+    // dc.  The matrix instruction takes bytes 0..15 of half-wave h as k = 16 h +
+    // 0..15 and bytes 16..31 as k = 32 + 16 h + 0..15; any placement shared by Q
+    // and K gives the same product, and the MX variant needs k = d - 64 dc, so
+    // that each 32-element scale block is one group of 32 coordinates.  Without
+    // MX the lane holds d = 64 dc + 32 half + 0..31, with MX
+    // d = 64 dc + 16 half + 0..15 and 64 dc + 32 + 16 half + 0..15.
+    i32x8 qf[2];
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+      if (qi < N) {
+        const uint8_t* row = Q8 + hoff + (size_t)qi * D + 64 * dc;
+        u0 = *reinterpret_cast<const uint4*>(row + (MX ? 16 * half : 32 * half));
+        u1 = *reinterpret_cast<const uint4*>(row + (MX ? 32 + 16 * half : 32 * half + 16));
+      }
+      qf[dc] = i32x8{(int)(u0.x ^ qflip), (int)(u0.y ^ qflip), (int)(u0.z ^ qflip), (int)(u0.w ^ qflip),
+                     (int)(u1.x ^ qflip), (int)(u1.y ^ qflip), (int)(u1.z ^ qflip), (int)(u1.w ^ qflip)};
     }
-    if (MX && wave == 0) lds_dma4(kmxrs, &kmxs[MX ? BUF : 0][0], 4 * lane, (uint32_t)j0 * 4);   // 64 keys x 4 B
-  };
 
-  f32x16 acc[4];
+    // MX: this query's four E8M0 scales, shifted so that byte 2 dc holds the group of d-chunk dc
+    uint32_t qsc = 0;
+    if (MX) {
+      const uint32_t qmx = qi < N ? *reinterpret_cast<const uint32_t*>(QMX + ((size_t)bh * N + qi) * 4) : 0x7F7F7F7Fu;
+      qsc = qmx >> (8 * half);
+    }
+    const int kend = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kend + BC - 1) / BC;
+
+    const uint32_t nbytes = (uint32_t)N * D;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K8 + hoff), 0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V8 + hoff), 0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kmxrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? KMX + (size_t)bh * N * 4 : K8), 0, (uint32_t)N * 4, 0x00020000);
+    auto issue_tile = [&](int j0, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
+      const uint32_t base = (uint32_t)j0 * D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  float m2 = -INFINITY, lsum = 0.0f;
+      for (int i = 0; i < LPW; ++i) {
+        const int slot0 = (i * NW + wave) * 64;
+        lds_dma16(krs, &smem[BUF][0][slot0], lane_off[i], base);
+        lds_dma16(vrs, &smem[BUF][1][slot0], lane_off[i], base);
+      }
+      if (MX && wave == 0) lds_dma4(kmxrs, &kmxs[MX ? BUF : 0][0], 4 * lane, (uint32_t)j0 * 4);   // 64 keys x 4 B
+    };
 
-  auto step = [&](int t, const BlockK& bk, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int j0 = t * BC;
-    __builtin_amdgcn_s_waitcnt(VMCNT(0));
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
-    if (CAUSAL && j0 > qw + 31) return;
-    const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
-    const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
-    const uint32_t* km = &kmxs[MX ? BUF : 0][0];
-    if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
-      tile_math<CAUSAL, true, MX>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half, km, arow, qsc);
-    else
-      tile_math<CAUSAL, false, MX>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half, km, arow, qsc);
-  };
-
-  issue_tile(0, IC<0>{});
-  for (int t = 0; t < ntiles; t += 2) {       // tiles t and t + 1 share one 128-key scaling block
-    const BlockK bk = block_consts(c_q, ksh[t / 2], vsh[t / 2] / svmax);
-    step(t, bk, IC<0>{});
-    if (t + 1 < ntiles) step(t + 1, bk, IC<1>{});
-  }
-
-  // epilogue: O = acc max s_v / (256 l) (then H / sqrt(d) for the Hadamard
-  // variant of V), LSE = ln 2 * (m2 + log2 l)
-  const float ltot = wave_halves_sum(lsum);
-  if (VHAD) fwht_o(acc, half);               // every lane, before the row guard: the stage pairs lanes
-  if (qi < N) {
-    const float f = svmax / (256.0f * ltot) * (VHAD ? 0.08838834764831845f : 1.0f);   // 1 / sqrt(128)
-    uint16_t* orow = O + hoff + (size_t)qi * D;
-    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+    f32x16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * db + 8 * a + 4 * half;
-        const bf16x4_t w = {(__bf16)(acc[db][4 * a + 0] * f), (__bf16)(acc[db][4 * a + 1] * f),
-                            (__bf16)(acc[db][4 * a + 2] * f), (__bf16)(acc[db][4 * a + 3] * f)};
-        *reinterpret_cast<bf16x4_t*>(orow + d0) = w;
-      }
-    if (half == 0) LSE[(size_t)bh * N + qi] = (m2 + __log2f(ltot)) * 0.69314718055994531f;
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    float m2 = -INFINITY, lsum = 0.0f;
+
+    auto step = [&](int t, const BlockK& bk, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
+      const int j0 = t * BC;
+      __builtin_amdgcn_s_waitcnt(VMCNT(0));
+      __syncthreads();
+      if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
+      if (CAUSAL && j0 > qw + 31) return;
+      const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
+      const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);
+      const uint32_t* km = &kmxs[MX ? BUF : 0][0];
+      if ((j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw))
+        tile_math<CAUSAL, true, MX>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half, km, arow, qsc);
+      else
+        tile_math<CAUSAL, false, MX>(kt, vt, koff, voff, qf, acc, m2, lsum, bk, j0, qi, N, half, km, arow, qsc);
+    };
+
+    issue_tile(0, IC<0>{});
+    for (int t = 0; t < ntiles; t += 2) {       // tiles t and t + 1 share one 128-key scaling block
+      const BlockK bk = block_consts(c_q, ksh[t / 2], vsh[t / 2] / svmax);
+      step(t, bk, IC<0>{});
+      if (t + 1 < ntiles) step(t + 1, bk, IC<1>{});
+    }
+
+    // epilogue: O = acc max s_v / (256 l) (then H / sqrt(d) for the Hadamard
+    // variant of V), LSE = ln 2 * (m2 + log2 l)
+    const float ltot = wave_halves_sum(lsum);
+    if (VHAD) fwht_o(acc, half);               // every lane, before the row guard: the stage pairs lanes
+    if (qi < N) {
+      const float f = svmax / (256.0f * ltot) * (VHAD ? 0.08838834764831845f : 1.0f);   // 1 / sqrt(128)
+      uint16_t* orow = O + hoff + (size_t)qi * D;
+      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * db + 8 * a + 4 * half;
+          const bf16x4_t w = {(__bf16)(acc[db][4 * a + 0] * f), (__bf16)(acc[db][4 * a + 1] * f),
+                              (__bf16)(acc[db][4 * a + 2] * f), (__bf16)(acc[db][4 * a + 3] * f)};
+          *reinterpret_cast<bf16x4_t*>(orow + d0) = w;
+        }
+      if (half == 0) LSE[(size_t)bh * N + qi] = (m2 + __log2f(ltot)) * 0.69314718055994531f;
+    }
+    __syncthreads();                         // every wave is done with the tile buffers before the next item's DMA
   }
 }
 
@@ -446,11 +472,21 @@ hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const
                   const float* vs, const uint8_t* qmx, const uint8_t* kmx, void* o, float* lse, int B, int H, int N,
                   float scale, hipStream_t stream) {
   const int nqb = (N + BR - 1) / BR;
-  const int total = nqb * H * B;
+  const int BH = B * H;
+  const long total = (long)nqb * BH;
   const float c0 = (float)((double)__builtin_fabsf(scale) * 1.4426950408889634);
   const uint32_t qflip = scale < 0.0f ? 0x80808080u : 0u;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, MX, VHAD>), dim3(total), dim3(NT), 0, stream, q8, k8, v8, qs, ks,
-                     vs, qmx, kmx, static_cast<uint16_t*>(o), lse, N, nqb, total, c0, qflip);
+  // one persistent workgroup per resident slot, never more than there are items
+  const long slots = device_slots(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<CAUSAL, MX, VHAD>), NT);
+  if (slots <= 0) return hipErrorInvalidDevice;
+  int grid = total < slots ? (int)total : (int)slots;
+  int groups = 1;
+  if (BH % 8 == 0 && grid >= 8) {            // one head set per XCD
+    grid -= grid % 8;
+    groups = 8;
+  }
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, MX, VHAD>), dim3(grid), dim3(NT), 0, stream, q8, k8, v8, qs, ks,
+                     vs, qmx, kmx, static_cast<uint16_t*>(o), lse, N, nqb, BH, groups, c0, qflip);
   return hipGetLastError();
 }
 
