@@ -22,11 +22,11 @@
 //    less than half the byte rate.  All backward kernels stay clear of the
 //    LDS bandwidth limit this way (HBM cost: three bf16 copies, a few percent
 //    of the pass);
-//  * dK/dV pass: 4 waves (one per SIMD) own 128 keys, 32 each, with K and V in
-//    registers as B operands and the dK and dV accumulators in AGPRs; 32-query
-//    tiles of Q, dO, their d-major copies, LSE and Delta stream through LDS by
-//    DMA, double buffered.  Per tile: S = Q K^T, dP = dO V^T, P and dS, then
-//    dV^T += dO^T P and dK^T += Q^T dS.
+//  * dK/dV pass: 8 waves (two per SIMD) own 128 keys in four groups of 32.
+//    For each group one wave holds K and forms S, P and dV^T += dO^T P; the
+//    other holds V, forms dP and, one tile later, dS = P (dP - Delta) (P
+//    passed through LDS) and dK^T += Q^T dS.  32-query tiles of Q, dO, their
+//    d-major copies, LSE and Delta stream through LDS by DMA.
 //  * dQ pass: 8 waves of 32 queries (Q and dO in registers), 64-key tiles of
 //    K, V and K's d-major copy through LDS; per tile S^T = K Q^T,
 //    dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
@@ -121,18 +121,26 @@ __device__ __forceinline__ int tchunk(int d, int c) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV in one pass.  One workgroup = 4 waves, one per SIMD, owns 128 keys,
-// 32 per wave, with K and V of its keys in registers as the B operands of S and
-// dP.  At one wave per SIMD a wave may use 512 registers, and the compiler
-// keeps the matrix accumulators (dK, dV, S, dP: 160 per lane) in AGPRs; at two
-// waves per SIMD they would not fit.  32-query tiles of Q, dO, their d-major
-// copies, LSE and Delta stream through LDS by DMA, double buffered, from the
-// end of the sequence down: every workgroup of a head reads the same tile at
-// about the same time, so the head's query-side data passes through the XCD's
-// L2 once.  Per tile: S = Q K^T and dP = dO V^T (A operands: Q and dO rows,
-// permuted), P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS (A
-// operands from the d-major tiles).
-constexpr int KV_NT = 256;   // 4 waves, one per SIMD
+// dK and dV in one pass, split between two wave roles.  One workgroup = 8
+// waves, two per SIMD, owns 128 keys.  Waves 0..3 ("P waves") each own 32
+// keys with K in registers: per query tile they form S = Q K^T, P, store P
+// (float32) in LDS and add dV^T += dO^T P.  Waves 4..7 ("dS waves") own the
+// same four 32-key groups with V in registers: per tile they form dP = dO V^T
+// and keep dP - Delta in registers; one step later they read that tile's P,
+// form dS = P (dP - Delta) and add dK^T += Q^T dS.  Each wave holds one
+// accumulator set (64 registers, not 128), so two waves fit on every SIMD, one
+// of each role (hardware waves go to SIMDs round-robin: P wave w and dS wave
+// w + 4 share one), and one's softmax runs beside the other's matrix products.
+// Both roles compute P, dP and dS exactly as a single wave would.
+// 32-query tiles of Q, dO, their d-major copies, LSE and Delta stream through
+// LDS by DMA from the end of the sequence down (every workgroup of a head reads
+// the same tile at about the same time, so the head's query-side data passes
+// through the XCD's L2 once).  Every buffer has two slots, each its own
+// __shared__ object, and the unrolled loops name the slot at compile time: the
+// compiler then knows that reading one slot does not alias the DMA in flight
+// into the other, and only the step barrier waits for the DMA.  The d-major Q
+// tile, which the dS waves use one step late, is fetched one step late too.
+constexpr int KV_NT = 512;   // 8 waves, two per SIMD
 constexpr int KV_KW = 32;    // keys per wave
 constexpr int KV_BK = 128;   // keys per workgroup
 constexpr int KV_TQ = 32;    // queries per tile
@@ -147,32 +155,44 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
   constexpr int NW = KV_NT / 64;
   constexpr int ROW_CHUNKS = KV_TQ * CPR;
   constexpr int T_CHUNKS = D * (KV_TQ / 8);
+  constexpr int P_CHUNKS = 4 * KV_KW * KV_TQ / 4;          // float32 P of the four 32-key groups
   constexpr int RPW = (ROW_CHUNKS + KV_NT - 1) / KV_NT;   // DMA instructions per wave and row tile
   constexpr int TPW = (T_CHUNKS + KV_NT - 1) / KV_NT;
-  __shared__ uint4 qbuf0[ROW_CHUNKS], qbuf1[ROW_CHUNKS], obuf0[ROW_CHUNKS], obuf1[ROW_CHUNKS];
-  __shared__ uint4 qtb0[T_CHUNKS], qtb1[T_CHUNKS], otb0[T_CHUNKS], otb1[T_CHUNKS];
-  __shared__ float lbuf0[KV_TQ], lbuf1[KV_TQ], dbuf0[KV_TQ], dbuf1[KV_TQ];
+  __shared__ uint4 qr0[ROW_CHUNKS], qr1[ROW_CHUNKS], or0[ROW_CHUNKS], or1[ROW_CHUNKS];
+  __shared__ uint4 ot0[T_CHUNKS], ot1[T_CHUNKS], qt0[T_CHUNKS], qt1[T_CHUNKS];
+  __shared__ uint4 pb0[P_CHUNKS], pb1[P_CHUNKS];
+  __shared__ float lb0[KV_TQ], lb1[KV_TQ], db0[KV_TQ], db1[KV_TQ];
+  // slot S of each buffer, S known at compile time
+  auto QR = [&](auto sc) { return reinterpret_cast<char*>(decltype(sc)::value ? qr1 : qr0); };
+  auto OR = [&](auto sc) { return reinterpret_cast<char*>(decltype(sc)::value ? or1 : or0); };
+  auto OT = [&](auto sc) { return reinterpret_cast<char*>(decltype(sc)::value ? ot1 : ot0); };
+  auto QTB = [&](auto sc) { return reinterpret_cast<char*>(decltype(sc)::value ? qt1 : qt0); };
+  auto PB = [&](auto sc) { return reinterpret_cast<char*>(decltype(sc)::value ? pb1 : pb0); };
+  auto LB = [&](auto sc) { return decltype(sc)::value ? lb1 : lb0; };
+  auto DB = [&](auto sc) { return decltype(sc)::value ? db1 : db0; };
 
   const int L = xcd_logical_id(blockIdx.x, total);
   const int bh = L / nkb;
   const int k0 = (L - bh * nkb) * KV_BK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pwave = wave < 4;
+  const int grp = wave & 3;                  // 32-key group, shared by P wave grp and dS wave grp + 4
   const int half = lane >> 5, l32 = lane & 31;
-  const int kw0 = k0 + KV_KW * wave;
+  const int kw0 = k0 + KV_KW * grp;
   const int key = kw0 + l32;
   const size_t hoff = (size_t)bh * N * D;
   const uint32_t nbytes = (uint32_t)N * D * 2;
 
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K (P waves) or V (dS waves) of this wave's keys: the B operand of S or dP
+  bf16x8 kv[D / 16];
   {
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + hoff), 0, nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + hoff), 0, nbytes, 0x00020000);
+    const uint16_t* src = pwave ? K : V;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + hoff), 0, nbytes, 0x00020000);
     const uint32_t off = (uint32_t)(key * D + 8 * half) * 2;
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      kf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32 * dc, 0, 0));
-      vf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 32 * dc, 0, 0));
-    }
+    for (int dc = 0; dc < D / 16; ++dc)
+      kv[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * dc, 0, 0));
   }
   uint32_t koff[D / 16];
 #pragma unroll
@@ -180,6 +200,9 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
   uint32_t toff[2];
 #pragma unroll
   for (int qc = 0; qc < 2; ++qc) toff[qc] = 16 * tchunk<KV_TQ>(l32, 2 * qc + half);
+  // this lane's float32 P values 4 j .. 4 j + 3 of its group's tile: lane-linear,
+  // so the stores and loads of a wave each cover 1 KB of consecutive bytes
+  const uint32_t poff = grp * (KV_KW * KV_TQ * 4) + 16 * lane;
 
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + hoff), 0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + hoff), 0, nbytes, 0x00020000);
@@ -202,120 +225,225 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
     const int slot = (i * NW + wave) * 64 + lane, d = slot / (KV_TQ / 8), cc = slot % (KV_TQ / 8);
     t_off[i] = (uint32_t)(d * TT * 2 + 16 * (cc ^ ((d >> 2) & 3)));
   }
-  auto issue_tile = [&](int q0, uint4* qd, uint4* od, uint4* qtd, uint4* otd, float* ld, float* dd) {
+  const int qstart = CAUSAL ? k0 : 0;
+  const int ntiles = (N - qstart + KV_TQ - 1) / KV_TQ;
+  const int qtop = qstart + (ntiles - 1) * KV_TQ;
+  auto tile_q0 = [&](int t) { return qtop - t * KV_TQ; };
+  auto tile_tb = [&](int t) { return (uint32_t)((tile_q0(t) / TT) * D * TT + tile_q0(t) % TT) * 2; };
+  // rows of Q and dO, d-major dO, LSE and Delta of tile t into slot S
+  auto issue_rows = [&](auto sc, int t) {
+    const uint32_t rb = (uint32_t)tile_q0(t) * D * 2, tb = tile_tb(t);
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
       if ((i * NW + wave) * 64 < ROW_CHUNKS) {
-        lds_dma16(qrs, qd + (i * NW + wave) * 64, row_off[i], (uint32_t)q0 * D * 2);
-        lds_dma16(ors, od + (i * NW + wave) * 64, row_off[i], (uint32_t)q0 * D * 2);
+        lds_dma16(qrs, QR(sc) + 16 * (i * NW + wave) * 64, row_off[i], rb);
+        lds_dma16(ors, OR(sc) + 16 * (i * NW + wave) * 64, row_off[i], rb);
       }
-    const uint32_t tb = (uint32_t)((q0 / TT) * D * TT + q0 % TT) * 2;
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
-      if ((i * NW + wave) * 64 < T_CHUNKS) {
-        lds_dma16(qtrs, qtd + (i * NW + wave) * 64, t_off[i], tb);
-        lds_dma16(otrs, otd + (i * NW + wave) * 64, t_off[i], tb);
-      }
+      if ((i * NW + wave) * 64 < T_CHUNKS) lds_dma16(otrs, OT(sc) + 16 * (i * NW + wave) * 64, t_off[i], tb);
     if (wave == 0 && lane < KV_TQ / 4) {
-      lds_dma16(lrs, ld, 16 * lane, (uint32_t)q0 * 4);
-      lds_dma16(drs, dd, 16 * lane, (uint32_t)q0 * 4);
+      lds_dma16(lrs, LB(sc), 16 * lane, (uint32_t)tile_q0(t) * 4);
+      lds_dma16(drs, DB(sc), 16 * lane, (uint32_t)tile_q0(t) * 4);
     }
   };
+  // d-major Q of tile t into slot S
+  auto issue_qt = [&](auto sc, int t) {
+    const uint32_t tb = tile_tb(t);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      if ((i * NW + wave) * 64 < T_CHUNKS) lds_dma16(qtrs, QTB(sc) + 16 * (i * NW + wave) * 64, t_off[i], tb);
+  };
+  // start of step t (S = t % 2): wait for this wave's DMA and LDS stores, meet
+  // the other waves, then fetch the rows of tile t + 1 and the d-major Q of tile t
+  auto sync_issue = [&](auto sc, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+    __asm__ volatile("s_barrier" ::: "memory");
+    if (t + 1 < ntiles) issue_rows(IC<1 - S>{}, t + 1);
+    if (t < ntiles) issue_qt(sc, t);
+  };
 
-  f32x16 dka[D / 32], dva[D / 32];
+  f32x16 acc[D / 32];                        // dV^T (P waves) or dK^T (dS waves)
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dka[db][r] = 0.0f;
-      dva[db][r] = 0.0f;
-    }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  auto tile = [&](auto maskc, const char* qt, const char* ot, const char* qtt, const char* ott, const float* l2t,
-                  const float* dlt, int q0) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(maskc)::value;
-    f32x16 s, dp;
+  // P wave, tile t in slot S: S = Q K^T, P (stored), dV^T += dO^T P.  All of
+  // the tile's LDS operands are read first.  MASK (uniform) marks tiles that
+  // cross the diagonal or the end of the sequence; it guards only the zeroing
+  // of P, so both kinds of tile share one copy of the matrix code and the
+  // accumulators never change registers.
+  auto p_tile = [&](auto sc, bool mask, int q0) __attribute__((always_inline)) {
+    const char* qt = QR(sc);
+    const char* ott = OT(sc);
+    const float* l2t = LB(sc);
+    bf16x8 qa[D / 16], oa[2][D / 32];
+    float l2v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.0f;
-      dp[r] = 0.0f;
-    }
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + koff[dc]), kf[dc], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(ot + koff[dc]), vf[dc], dp, 0,
-                                                  0, 0);
-    }
+    for (int dc = 0; dc < D / 16; ++dc) qa[dc] = *reinterpret_cast<const bf16x8*>(qt + koff[dc]);
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       const float4 la = *reinterpret_cast<const float4*>(l2t + 16 * qc + 8 * half);
       const float4 lb = *reinterpret_cast<const float4*>(l2t + 16 * qc + 8 * half + 4);
-      const float4 da = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half);
-      const float4 dbv = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half + 4);
-      const float l2v[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-      const float dlv[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
-      bf16x8 pb, dsb;
+      l2v[8 * qc + 0] = la.x, l2v[8 * qc + 1] = la.y, l2v[8 * qc + 2] = la.z, l2v[8 * qc + 3] = la.w;
+      l2v[8 * qc + 4] = lb.x, l2v[8 * qc + 5] = lb.y, l2v[8 * qc + 6] = lb.z, l2v[8 * qc + 7] = lb.w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * qc + e], c, -l2v[e]));
-        if (MASK) {
-          const int q = q0 + 16 * qc + 8 * half + e;
-          if (key >= N || (CAUSAL && key > q)) p = 0.0f;
-        }
-        pb[e] = (__bf16)p;
-        dsb[e] = (__bf16)(p * (dp[8 * qc + e] - dlv[e]));
-      }
+      for (int db = 0; db < D / 32; ++db)
+        oa[qc][db] = *reinterpret_cast<const bf16x8*>(ott + toff[qc] + db * 32 * KV_TQ * 2);
+    }
+    f32x16 s;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(ott + toff[qc] + db * 32 * KV_TQ * 2), pb, dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(qtt + toff[qc] + db * 32 * KV_TQ * 2), dsb, dka[db], 0, 0, 0);
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], s, 0, 0, 0);
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2v[r]));
+    if (mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 16 * (r / 8) + 8 * half + r % 8;
+        if (key >= N || (CAUSAL && key > q)) p[r] = 0.0f;
       }
+    }
+    char* pw = PB(sc) + poff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(pw + 1024 * j) = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * qc + e];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[qc][db], pb, acc[db], 0, 0, 0);
     }
   };
 
-  const int qstart = CAUSAL ? k0 : 0;
-  const int ntiles = (N - qstart + KV_TQ - 1) / KV_TQ;
-  const int qtop = qstart + (ntiles - 1) * KV_TQ;
-  const bool active = kw0 < N;
-  const bool ktail = kw0 + KV_KW > N;
-  auto step = [&](int t, const uint4* qc, const uint4* oc, const uint4* qtc, const uint4* otc, const float* lc,
-                  const float* dlc, uint4* qn, uint4* on, uint4* qtn, uint4* otn, float* ln, float* dn)
+  // dS wave, step t (S = t % 2): dP of tile t (NEW, kept as dP - Delta in
+  // dnew) and dS and dK^T += Q^T dS of tile t - 1 (PREV, slot 1 - S, whose P
+  // the P waves stored one step earlier, with dP - Delta in dprev).  Both
+  // halves in one block, all LDS operands read first, so the compiler can
+  // interleave one tile's matrix products with the other's vector work.
+  auto ds_step = [&](auto sc, auto newc, auto prevc, f32x16& dnew, const f32x16& dprev)
       __attribute__((always_inline)) {
-    const int q0 = qtop - t * KV_TQ;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __asm__ volatile("s_barrier" ::: "memory");
-    if (t + 1 < ntiles) issue_tile(q0 - KV_TQ, qn, on, qtn, otn, ln, dn);
-    if (!active || (CAUSAL && q0 + KV_TQ - 1 < kw0)) return;
-    const char* qt = reinterpret_cast<const char*>(qc);
-    const char* ot = reinterpret_cast<const char*>(oc);
-    const char* qtt = reinterpret_cast<const char*>(qtc);
-    const char* ott = reinterpret_cast<const char*>(otc);
-    if (ktail || (CAUSAL && q0 < kw0 + KV_KW - 1)) tile(IC<1>{}, qt, ot, qtt, ott, lc, dlc, q0);
-    else tile(IC<0>{}, qt, ot, qtt, ott, lc, dlc, q0);
+    constexpr int S = decltype(sc)::value;
+    constexpr bool NEW = decltype(newc)::value, PREV = decltype(prevc)::value;
+    bf16x8 oa[D / 16], qa[2][D / 32];
+    float dl[16], pp[16];
+    if (NEW) {
+      const char* ot = OR(sc);
+      const float* dlt = DB(sc);
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) oa[dc] = *reinterpret_cast<const bf16x8*>(ot + koff[dc]);
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        const float4 da = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half);
+        const float4 dbv = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half + 4);
+        dl[8 * qc + 0] = da.x, dl[8 * qc + 1] = da.y, dl[8 * qc + 2] = da.z, dl[8 * qc + 3] = da.w;
+        dl[8 * qc + 4] = dbv.x, dl[8 * qc + 5] = dbv.y, dl[8 * qc + 6] = dbv.z, dl[8 * qc + 7] = dbv.w;
+      }
+    }
+    if (PREV) {
+      const char* qtt = QTB(IC<1 - S>{});
+      const char* pr = PB(IC<1 - S>{}) + poff;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(pr + 1024 * j);
+        pp[4 * j] = v.x, pp[4 * j + 1] = v.y, pp[4 * j + 2] = v.z, pp[4 * j + 3] = v.w;
+      }
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          qa[qc][db] = *reinterpret_cast<const bf16x8*>(qtt + toff[qc] + db * 32 * KV_TQ * 2);
+    }
+    f32x16 dp;
+    if (NEW) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dc], kv[dc], dp, 0, 0, 0);
+    }
+    if (PREV) {
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        bf16x8 dsb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsb[e] = (__bf16)(pp[8 * qc + e] * dprev[8 * qc + e]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qc][db], dsb, acc[db], 0, 0, 0);
+      }
+    }
+    if (NEW) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dnew[r] = dp[r] - dl[r];
+    }
   };
-  issue_tile(qtop, qbuf0, obuf0, qtb0, otb0, lbuf0, dbuf0);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, qbuf0, obuf0, qtb0, otb0, lbuf0, dbuf0, qbuf1, obuf1, qtb1, otb1, lbuf1, dbuf1);
-    if (t + 1 < ntiles)
-      step(t + 1, qbuf1, obuf1, qtb1, otb1, lbuf1, dbuf1, qbuf0, obuf0, qtb0, otb0, lbuf0, dbuf0);
+
+  // Every wave takes every tile of its workgroup's query range: a tile wholly
+  // above a wave's part of the diagonal gives P = 0 and adds exact zeros, and
+  // such tiles are about 1 % of the work.  With no per-wave skipping the loop
+  // bodies have no data-dependent branches around the matrix code.
+  const bool ktail = kw0 + KV_KW > N;
+  auto pmask = [&](int t) { return ktail || (CAUSAL && tile_q0(t) < kw0 + KV_KW - 1); };
+  issue_rows(IC<0>{}, 0);
+  if (pwave) {
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      sync_issue(IC<0>{}, t);
+      p_tile(IC<0>{}, pmask(t), tile_q0(t));
+      sync_issue(IC<1>{}, t + 1);
+      p_tile(IC<1>{}, pmask(t + 1), tile_q0(t + 1));
+    }
+    if (t < ntiles) {                        // t = ntiles - 1, even
+      sync_issue(IC<0>{}, t);
+      p_tile(IC<0>{}, pmask(t), tile_q0(t));
+      sync_issue(IC<1>{}, ntiles);           // the dS waves' last step reads the last P
+    } else {
+      sync_issue(IC<0>{}, ntiles);
+    }
+  } else {
+    // steps 0 .. ntiles: dP of tile t and dK of tile t - 1; d0 and d1
+    // alternate as the two tiles' dP - Delta
+    f32x16 d0, d1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) d1[r] = 0.0f;
+    sync_issue(IC<0>{}, 0);
+    ds_step(IC<0>{}, IC<1>{}, IC<0>{}, d0, d1);
+    int t = 1;
+    for (; t + 1 < ntiles; t += 2) {
+      sync_issue(IC<1>{}, t);
+      ds_step(IC<1>{}, IC<1>{}, IC<1>{}, d1, d0);
+      sync_issue(IC<0>{}, t + 1);
+      ds_step(IC<0>{}, IC<1>{}, IC<1>{}, d0, d1);
+    }
+    if (t < ntiles) {                        // t odd, ntiles = t + 1
+      sync_issue(IC<1>{}, t);
+      ds_step(IC<1>{}, IC<1>{}, IC<1>{}, d1, d0);
+      sync_issue(IC<0>{}, ntiles);
+      ds_step(IC<0>{}, IC<0>{}, IC<1>{}, d0, d1);
+    } else {                                 // t = ntiles, odd
+      sync_issue(IC<1>{}, ntiles);
+      ds_step(IC<1>{}, IC<0>{}, IC<1>{}, d1, d0);
+    }
   }
   if (key < N) {
-    uint16_t* krow = dK + hoff + (size_t)key * D;
-    uint16_t* vrow = dV + hoff + (size_t)key * D;
+    uint16_t* row = (pwave ? dV : dK) + hoff + (size_t)key * D;
+    const float f = pwave ? 1.0f : scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = 32 * db + 8 * a + 4 * half;
-        const bf16x4_t wk = {(__bf16)(dka[db][4 * a + 0] * scale), (__bf16)(dka[db][4 * a + 1] * scale),
-                             (__bf16)(dka[db][4 * a + 2] * scale), (__bf16)(dka[db][4 * a + 3] * scale)};
-        const bf16x4_t wv = {(__bf16)dva[db][4 * a + 0], (__bf16)dva[db][4 * a + 1], (__bf16)dva[db][4 * a + 2],
-                             (__bf16)dva[db][4 * a + 3]};
-        *reinterpret_cast<bf16x4_t*>(krow + d0) = wk;
-        *reinterpret_cast<bf16x4_t*>(vrow + d0) = wv;
+        const bf16x4_t w = {(__bf16)(acc[db][4 * a + 0] * f), (__bf16)(acc[db][4 * a + 1] * f),
+                            (__bf16)(acc[db][4 * a + 2] * f), (__bf16)(acc[db][4 * a + 3] * f)};
+        *reinterpret_cast<bf16x4_t*>(row + d0) = w;
       }
   }
 }
