@@ -297,10 +297,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace        : device memory owned by the caller, at least
  *                      fa_bwd_workspace_bytes(B,H,N,d) bytes (FA_ERR_ARG
  *                      otherwise); it receives Delta and LSE log2(e), float32
- *                      [B,H,N] each, and d-major bf16 copies of Q, dO and K in
- *                      64-token tiles (about 3 B*H*N*d*2 bytes in all).  Calls
- *                      that share a workspace must not run concurrently.
- * Four kernels on `stream`; the results are deterministic (no atomics).
+ *                      [B,H,N] each (8 B*H*N bytes, rounded up).  Calls that
+ *                      share a workspace must not run concurrently.
+ * Three kernels on `stream`; the results are deterministic (no atomics).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
