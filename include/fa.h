@@ -299,7 +299,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                      otherwise); it receives Delta and LSE log2(e), float32
  *                      [B,H,N] each (8 B*H*N bytes, rounded up).  Calls that
  *                      share a workspace must not run concurrently.
- * Three kernels on `stream`; the results are deterministic (no atomics).
+ * Two kernels on `stream`; the results are deterministic (no atomics).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,

@@ -12,16 +12,16 @@
 // As in the forward, no N x N matrix is ever written to HBM: S, P, dP and dS
 // exist one register tile at a time.
 //
-// Kernels on the caller's stream:
-//  * Delta pass: Delta_i = sum_d dO_id O_id and LSE_i log2(e);
-//  * dK/dV pass: 8 waves (two per SIMD) own 128 keys in four groups of 32.
+// Kernels on the caller's stream, in this order:
+//  * dQ pass: 8 waves of 32 queries (Q and dO in registers), 64-key tiles of
+//    K and V rows through LDS; per tile S^T = K Q^T, dP^T = V dO^T, dS^T,
+//    dQ^T += K^T dS^T.  It also forms Delta_i = dO_i . O_i and LSE_i log2(e)
+//    of its queries and leaves them in the workspace for
+//  * the dK/dV pass: 8 waves (two per SIMD) own 128 keys in four groups of 32.
 //    For each group one wave holds K and forms S, P and dV^T += dO^T P; the
 //    other holds V, forms dP, then dS = P (dP - Delta) (P passed through LDS)
 //    and dK^T += Q^T dS.  32-query tiles of Q and dO rows, LSE and Delta
 //    stream through LDS by DMA.
-//  * dQ pass: 8 waves of 32 queries (Q and dO in registers), 64-key tiles of
-//    K and V rows through LDS; per tile S^T = K Q^T, dP^T = V dO^T, dS^T,
-//    dQ^T += K^T dS^T.
 // A product that sums over tokens (dV = P^T dO, dK = dS^T Q, dQ = dS K) needs
 // its A operand with 8 consecutive tokens per lane; it comes from the row
 // tile in LDS through transposing reads (ds_read_b64_tr_b16), as the forward
@@ -42,36 +42,6 @@ namespace {
 using namespace bf16k;
 
 constexpr float LOG2E = 1.4426950408889634f;
-
-// ---------------------------------------------------------------------------
-// prep: Delta and LSE * log2(e), float32 [B*H*N]
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const uint16_t* __restrict__ O,
-                                                            const uint16_t* __restrict__ dO,
-                                                            const float* __restrict__ LSE, float* __restrict__ L2,
-                                                            float* __restrict__ Dl, long rows) {
-  constexpr int LPR = D / 8;              // lanes per row, 8 elements each
-  constexpr int RPB = 256 / LPR;          // rows per workgroup
-  const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
-  float acc = 0.0f;
-  if (row < rows) {
-    const uint4 a = *reinterpret_cast<const uint4*>(O + row * D + 8 * sub);
-    const uint4 b = *reinterpret_cast<const uint4*>(dO + row * D + 8 * sub);
-    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = __builtin_fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(av[i] & 0xFFFF0000u), __uint_as_float(bv[i] & 0xFFFF0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row < rows && sub == 0) {
-    Dl[row] = acc;
-    L2[row] = LSE[row] * LOG2E;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK and dV in one pass, split between two wave roles.  One workgroup = 8
@@ -379,8 +349,9 @@ constexpr int DQ_BR = 256;   // queries per workgroup
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DQ_NT, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
-    uint16_t* __restrict__ dQ, int N, int nqb, int total, float c, float scale) {
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ L2, float* __restrict__ Dl, uint16_t* __restrict__ dQ, int N, int nqb, int total, float c,
+    float scale) {
   constexpr int CPR = D / 8;
   constexpr int NW = DQ_NT / 64;
   constexpr int TILE_CHUNKS = BC * CPR;            // row-major 64-key tile
@@ -403,18 +374,32 @@ __global__ __launch_bounds__(DQ_NT, 1) void attn_bwd_dq_kernel(
 
   // Q^T and dO^T as B operands: lane holds query qi, dims 16 dc + 8 half + 0..7
   bf16x8 qf[D / 16], of[D / 16];
+  float dl = 0.0f;                           // Delta of query qi, this lane's half of the dims first
   {
     const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + hoff), 0, nbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + hoff), 0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)(O + hoff), 0, nbytes, 0x00020000);
     const uint32_t off = (uint32_t)(qi * D + 8 * half) * 2;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
       qf[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 32 * dc, 0, 0));
       of[dc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ors, off + 32 * dc, 0, 0));
     }
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 32 * dc, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl = __builtin_fmaf((float)of[dc][e], (float)o8[e], dl);
+    }
   }
-  const float l2 = qi < N ? L2[(size_t)bh * N + qi] : 0.0f;
-  const float dl = qi < N ? Dl[(size_t)bh * N + qi] : 0.0f;
+  // Delta_i = dO_i . O_i and LSE_i log2(e) of this wave's queries, which the
+  // dK/dV pass (launched after this one) reads from the workspace
+  dl = wave_halves_sum(dl);
+  const float l2 = qi < N ? LSE[(size_t)bh * N + qi] * LOG2E : 0.0f;
+  if (qi < N && half == 0) {
+    L2[(size_t)bh * N + qi] = l2;
+    Dl[(size_t)bh * N + qi] = dl;
+  }
 
   // LDS byte offsets: K / V rows (A operand of S^T and dP^T, rows permuted)
   // and the transposing reads of K^T (A operand of dQ^T: rows d of block db,
@@ -564,27 +549,22 @@ Ws carve(void* base, int B, int H, int N) {
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, const Ws& w, int B, int H, int N, float scale, hipStream_t stream) {
-  const long rows = (long)B * H * N;
-  constexpr int RPB = 256 / (D / 8);
   const auto* Q = static_cast<const uint16_t*>(q);
   const auto* K = static_cast<const uint16_t*>(k);
   const auto* V = static_cast<const uint16_t*>(v);
   const auto* dO = static_cast<const uint16_t*>(dout);
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(o), dO, lse, w.l2, w.dl, rows);
+  const float c = (float)((double)scale * 1.4426950408889634);
+  const int nqb = (N + DQ_BR - 1) / DQ_BR;
+  const int tq = nqb * B * H;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(tq), dim3(DQ_NT), 0, stream, Q, K, V, dO,
+                     static_cast<const uint16_t*>(o), lse, w.l2, w.dl, static_cast<uint16_t*>(dq), N, nqb, tq, c,
+                     scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const float c = (float)((double)scale * 1.4426950408889634);
   const int nkb = (N + KV_BK - 1) / KV_BK;
   const int tkv = nkb * B * H;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3(tkv), dim3(KV_NT), 0, stream, Q, K, V, dO, w.l2, w.dl,
                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, nkb, tkv, c, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nqb = (N + DQ_BR - 1) / DQ_BR;
-  const int tq = nqb * B * H;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(tq), dim3(DQ_NT), 0, stream, Q, K, V, dO, w.l2, w.dl,
-                     static_cast<uint16_t*>(dq), N, nqb, tq, c, scale);
   return hipGetLastError();
 }
 
