@@ -20,7 +20,7 @@
 //  * the dK/dV pass: 8 waves (two per SIMD) own 128 keys in four groups of 32.
 //    For each group one wave holds K and forms S, P and dV^T += dO^T P; the
 //    other holds V, forms dP, then dS = P (dP - Delta) (P passed through LDS)
-//    and dK^T += Q^T dS.  32-query tiles of Q and dO rows, LSE and Delta
+//    and dK^T += Q^T dS.  64-query tiles of Q and dO rows, LSE and Delta
 //    stream through LDS by DMA.
 // A product that sums over tokens (dV = P^T dO, dK = dS^T Q, dQ = dS K) needs
 // its A operand with 8 consecutive tokens per lane; it comes from the row
@@ -51,7 +51,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 // registers, not 128), so two waves fit on every SIMD, one of each role
 // (hardware waves go to SIMDs round-robin: P wave w and dS wave w + 4 share
 // one), and one's vector work runs beside the other's matrix products.  Per
-// 32-query tile, two phases split by a barrier:
+// 64-query tile, two phases split by a barrier (each handles the tile in
+// two 32-query halves):
 //   1. P waves: S = Q K^T, P (stored to LDS as float32);
 //      dS waves: dP = dO V^T, kept as dP - Delta;
 //   2. P waves: dV^T += dO^T P;  dS waves: dS = P (dP - Delta), dK^T += Q^T dS.
@@ -67,7 +68,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int KV_NT = 512;   // 8 waves, two per SIMD
 constexpr int KV_KW = 32;    // keys per wave
 constexpr int KV_BK = 128;   // keys per workgroup
-constexpr int KV_TQ = 32;    // queries per tile
+constexpr int KV_TQ = 64;    // queries per tile
+constexpr int KV_NH = KV_TQ / 32;   // 32-query halves of a tile
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
@@ -77,8 +79,10 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
   constexpr int CPR = D / 8;
   constexpr int ROW_CHUNKS = KV_TQ * CPR;
   constexpr int P_CHUNKS = 4 * KV_KW * KV_TQ / 4;          // float32 P of the four 32-key groups
+  constexpr int KB_BYTES = 32 * D * 2;                     // 32 query rows of a row tile
   constexpr int KC_BYTES = 16 * D * 2;                     // 16 query rows of a row tile
-  static_assert(ROW_CHUNKS <= KV_NT, "one DMA instruction per wave and tensor");
+  constexpr int RPW = ROW_CHUNKS / KV_NT;                  // DMA instructions per wave and tensor
+  static_assert(ROW_CHUNKS % KV_NT == 0, "whole DMA instructions per wave and tensor");
   __shared__ uint4 qr0[ROW_CHUNKS], qr1[ROW_CHUNKS], or0[ROW_CHUNKS], or1[ROW_CHUNKS];
   __shared__ float lb0[KV_TQ], lb1[KV_TQ], db0[KV_TQ], db1[KV_TQ];
   __shared__ uint4 pbuf[P_CHUNKS];
@@ -136,11 +140,11 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
   // past the end read as zeros.  (A VGPR that addressed a DMA in flight is
   // not rewritten before that DMA completes, so per-tile vector offsets could
   // make the compiler wait for the prefetch.)
-  const bool dma_wave = wave * 64 < ROW_CHUNKS;
-  uint32_t row_off;
-  {
-    const int r = tid / CPR, ch = tid % CPR;
-    row_off = (uint32_t)(r * D + 8 * (ch ^ swz<D>(r))) * 2;
+  uint32_t row_off[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int slot = i * KV_NT + tid, r = slot / CPR, ch = slot % CPR;
+    row_off[i] = (uint32_t)(r * D + 8 * (ch ^ swz<D>(r))) * 2;
   }
   const uint32_t lane_off = 16 * lane;
   const char* qh = reinterpret_cast<const char*>(Q + hoff);
@@ -158,9 +162,10 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
   auto issue_tile = [&](auto sc, int t) {
     constexpr int S = decltype(sc)::value;
     const uint32_t rb = (uint32_t)tile_q0(t) * D * 2;
-    if (dma_wave) {
-      lds_dma16(rsrc_at(qh, rb, nbytes), (S ? qr1 : qr0) + 64 * wave, row_off, 0);
-      lds_dma16(rsrc_at(oh, rb, nbytes), (S ? or1 : or0) + 64 * wave, row_off, 0);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      lds_dma16(rsrc_at(qh, rb, nbytes), (S ? qr1 : qr0) + i * KV_NT + 64 * wave, row_off[i], 0);
+      lds_dma16(rsrc_at(oh, rb, nbytes), (S ? or1 : or0) + i * KV_NT + 64 * wave, row_off[i], 0);
     }
     if (wave == 0 && lane < KV_TQ / 4) {
       const uint32_t lb = (uint32_t)tile_q0(t) * 4;
@@ -175,11 +180,12 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  // acc[db] += A^T B over the tile's 32 queries, A^T read transposed from the
-  // row tile at rt (dO rows for dV, Q rows for dK), B = b[qc] (P or dS)
-  auto tr_products = [&](const char* rt, const bf16x8 (&b)[2]) __attribute__((always_inline)) {
+  // acc[db] += A^T B over the tile's queries, A^T read transposed from the
+  // row tile at rt (dO rows for dV, Q rows for dK), B = b[qc] (P or dS) for
+  // queries 16 qc .. 16 qc + 15
+  auto tr_products = [&](const char* rt, const bf16x8 (&b)[2 * KV_NH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qc = 0; qc < 2; ++qc)
+    for (int qc = 0; qc < 2 * KV_NH; ++qc)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const bf16x4_t v0 = tr_read(rt + voff[db][0] + qc * KC_BYTES);
@@ -189,86 +195,97 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
       }
   };
 
-  // P wave, phase 1 of tile t (slot S): S = Q K^T, P (stored); returns P as
-  // the bf16 B operands of phase 2.  MASK (uniform) marks tiles that cross the
-  // diagonal or the end of the sequence; it guards only the zeroing of P, so
-  // both kinds of tile share one copy of the matrix code.
-  auto p_phase1 = [&](auto sc, bool mask, int q0, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+  // P wave, phase 1 of tile t (slot S): S = Q K^T, P (stored), one 32-query
+  // half at a time; returns P as the bf16 B operands of phase 2.  MASK
+  // (uniform) marks tiles that cross the diagonal or the end of the sequence;
+  // it guards only the zeroing of P, so both kinds of tile share one copy of
+  // the matrix code.
+  auto p_phase1 = [&](auto sc, bool mask, int q0, bf16x8 (&pb)[2 * KV_NH]) __attribute__((always_inline)) {
     const char* qt = QR(sc);
     const float* l2t = LB(sc);
-    bf16x8 qa[D / 16];
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) qa[dc] = *reinterpret_cast<const bf16x8*>(qt + koff[dc]);
-    float l2v[16];
+    for (int h = 0; h < KV_NH; ++h) {
+      bf16x8 qa[D / 16];
 #pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
-      const float4 la = *reinterpret_cast<const float4*>(l2t + 16 * qc + 8 * half);
-      const float4 lb = *reinterpret_cast<const float4*>(l2t + 16 * qc + 8 * half + 4);
-      l2v[8 * qc + 0] = la.x, l2v[8 * qc + 1] = la.y, l2v[8 * qc + 2] = la.z, l2v[8 * qc + 3] = la.w;
-      l2v[8 * qc + 4] = lb.x, l2v[8 * qc + 5] = lb.y, l2v[8 * qc + 6] = lb.z, l2v[8 * qc + 7] = lb.w;
-    }
-    f32x16 s;
+      for (int dc = 0; dc < D / 16; ++dc) qa[dc] = *reinterpret_cast<const bf16x8*>(qt + h * KB_BYTES + koff[dc]);
+      float l2v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], s, 0, 0, 0);
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2v[r]));
-    if (mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 16 * (r / 8) + 8 * half + r % 8;
-        if (key >= N || (CAUSAL && key > q)) p[r] = 0.0f;
+      for (int qc = 0; qc < 2; ++qc) {
+        const float4 la = *reinterpret_cast<const float4*>(l2t + 32 * h + 16 * qc + 8 * half);
+        const float4 lb = *reinterpret_cast<const float4*>(l2t + 32 * h + 16 * qc + 8 * half + 4);
+        l2v[8 * qc + 0] = la.x, l2v[8 * qc + 1] = la.y, l2v[8 * qc + 2] = la.z, l2v[8 * qc + 3] = la.w;
+        l2v[8 * qc + 4] = lb.x, l2v[8 * qc + 5] = lb.y, l2v[8 * qc + 6] = lb.z, l2v[8 * qc + 7] = lb.w;
       }
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], s, 0, 0, 0);
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2v[r]));
+      if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + 32 * h + 16 * (r / 8) + 8 * half + r % 8;
+          if (key >= N || (CAUSAL && key > q)) p[r] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(pw + 1024 * (4 * h + j)) =
+            make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[2 * h + qc][e] = (__bf16)p[8 * qc + e];
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(pw + 1024 * j) = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
-#pragma unroll
-    for (int qc = 0; qc < 2; ++qc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[qc][e] = (__bf16)p[8 * qc + e];
   };
 
   // dS wave, phase 1 of tile t (slot S): dP = dO V^T, returned as dP - Delta
-  auto d_phase1 = [&](auto sc, f32x16& dpm) __attribute__((always_inline)) {
+  auto d_phase1 = [&](auto sc, f32x16 (&dpm)[KV_NH]) __attribute__((always_inline)) {
     const char* ot = OR(sc);
     const float* dlt = DB(sc);
-    bf16x8 oa[D / 16];
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) oa[dc] = *reinterpret_cast<const bf16x8*>(ot + koff[dc]);
-    float dl[16];
+    for (int h = 0; h < KV_NH; ++h) {
+      bf16x8 oa[D / 16];
 #pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
-      const float4 da = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half);
-      const float4 dbv = *reinterpret_cast<const float4*>(dlt + 16 * qc + 8 * half + 4);
-      dl[8 * qc + 0] = da.x, dl[8 * qc + 1] = da.y, dl[8 * qc + 2] = da.z, dl[8 * qc + 3] = da.w;
-      dl[8 * qc + 4] = dbv.x, dl[8 * qc + 5] = dbv.y, dl[8 * qc + 6] = dbv.z, dl[8 * qc + 7] = dbv.w;
+      for (int dc = 0; dc < D / 16; ++dc) oa[dc] = *reinterpret_cast<const bf16x8*>(ot + h * KB_BYTES + koff[dc]);
+      float dl[16];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        const float4 da = *reinterpret_cast<const float4*>(dlt + 32 * h + 16 * qc + 8 * half);
+        const float4 dbv = *reinterpret_cast<const float4*>(dlt + 32 * h + 16 * qc + 8 * half + 4);
+        dl[8 * qc + 0] = da.x, dl[8 * qc + 1] = da.y, dl[8 * qc + 2] = da.z, dl[8 * qc + 3] = da.w;
+        dl[8 * qc + 4] = dbv.x, dl[8 * qc + 5] = dbv.y, dl[8 * qc + 6] = dbv.z, dl[8 * qc + 7] = dbv.w;
+      }
+      f32x16 dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dc], kv[dc], dp, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpm[h][r] = dp[r] - dl[r];
     }
-    f32x16 dp;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dc], kv[dc], dp, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dpm[r] = dp[r] - dl[r];
   };
 
   // dS wave, phase 2: dS = P (dP - Delta) with the P the P wave just stored,
   // then dK^T += Q^T dS
-  auto d_phase2 = [&](auto sc, const f32x16& dpm) __attribute__((always_inline)) {
-    float pp[16];
+  auto d_phase2 = [&](auto sc, const f32x16 (&dpm)[KV_NH]) __attribute__((always_inline)) {
+    bf16x8 dsb[2 * KV_NH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(pw + 1024 * j);
-      pp[4 * j] = v.x, pp[4 * j + 1] = v.y, pp[4 * j + 2] = v.z, pp[4 * j + 3] = v.w;
+    for (int h = 0; h < KV_NH; ++h) {
+      float pp[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(pw + 1024 * (4 * h + j));
+        pp[4 * j] = v.x, pp[4 * j + 1] = v.y, pp[4 * j + 2] = v.z, pp[4 * j + 3] = v.w;
+      }
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsb[2 * h + qc][e] = (__bf16)(pp[8 * qc + e] * dpm[h][8 * qc + e]);
     }
-    bf16x8 dsb[2];
-#pragma unroll
-    for (int qc = 0; qc < 2; ++qc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dsb[qc][e] = (__bf16)(pp[8 * qc + e] * dpm[8 * qc + e]);
     tr_products(QR(sc), dsb);
   };
 
@@ -296,14 +313,14 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
   auto pstep = [&](auto sc, int t) __attribute__((always_inline)) {
     phase1(sc, t);
     const int q0 = tile_q0(t);
-    bf16x8 pb[2];
+    bf16x8 pb[2 * KV_NH];
     p_phase1(sc, ktail || (CAUSAL && q0 < kw0 + KV_KW - 1), q0, pb);
     phase2();
     tr_products(OR(sc), pb);
   };
   auto dstep = [&](auto sc, int t) __attribute__((always_inline)) {
     phase1(sc, t);
-    f32x16 dpm;
+    f32x16 dpm[KV_NH];
     d_phase1(sc, dpm);
     phase2();
     d_phase2(sc, dpm);
