@@ -16,18 +16,23 @@
 //    the tile: c_t = |scale| log2(e) s_q s_k.
 //  * P is quantised to E4M3 for the second product jointly with the V-block
 //    scale relative to the head's largest: s_v / max s_v = 2^E r with
-//    E = ceil(log2 of the ratio) and 1/2 < r <= 1; P holds E4M3(256 p r) and
+//    E = ceil(log2 of the ratio) and 1/2 < r <= 1; P holds E4M3(128 p r) and
 //    the power of two 2^E goes in as the E8M0 block scale of the V operand of
 //    v_mfma_scale_f32_32x32x64_f8f6f4.  One accumulator serves every V block,
-//    256 p r stays in E4M3's normal range whatever the blocks' magnitudes (an
+//    128 p r stays in E4M3's normal range whatever the blocks' magnitudes (an
 //    all-zero block has s_v = 1), and in the block with the largest scale
-//    r = 1, so a row's largest weight is stored exactly.  The factor 256 r is
+//    r = 1, so a row's largest weight is stored exactly.  The factor 128 r is
 //    folded into the exp2 argument (no extra multiply), l accumulates
-//    p = P / (256 r) in float32, and O = acc max s_v / (256 l).  The per-block
-//    constants are formed once per 128-key block (two tiles).
+//    p = P / (128 r) in float32, and O = acc max s_v / (128 l).  The per-block
+//    constants are formed once per 128-key block (two tiles).  (A power-of-two
+//    factor only shifts E4M3's grid: 128 stores every normal-range weight as
+//    256 would; it moves the subnormal start from 2^-14 to 2^-13 of the
+//    reference and buys one more binade of slack below.)
 //  * The reference maximum moves only when a tile's maximum exceeds it by
-//    more than 0.8 in the exp2 domain, so p <= 2^0.8 and 256 p r <= 445.7,
-//    inside E4M3 range (448), and the O rescale is rare.
+//    more than 1.8 in the exp2 domain, so p <= 2^1.8 and 128 p r <= 445.7,
+//    inside E4M3 range (448).  On inputs with large outliers a wave's 32 rows
+//    moved it (and rescaled O) on about half of the tiles at a slack of 0.8;
+//    at 1.8 that is rare.
 //  * Layouts as in the bf16 kernel (S^T and O^T accumulators; per-lane
 //    softmax state).  32x32x64 FP8 MFMA operands: lane l holds row (col)
 //    l % 32; its bytes 0..15 are k = 16 (l / 32) + 0..15 and bytes 16..31 are
@@ -140,10 +145,13 @@ __device__ __forceinline__ void fwht_o(f32x16 (&acc)[4], int half) {
 }
 
 // Constants of one 128-key block: c_t = softmax constant with the Q and K
-// block scales folded in; lr = log2(256 r); inv_r = 1 / (256 r); ve = E8M0
+// block scales folded in; lr = log2(P_SCALE r); inv_r = 1 / (P_SCALE r); ve = E8M0
 // code of 2^E, where s_v / max s_v = 2^E r, 1/2 < r <= 1.  A ratio below
 // 2^-127 leaves part of its magnitude in r, which then loses precision in P's
 // subnormals (such a block's contribution is below 2^-118 of the largest).
+constexpr float P_SCALE = 128.0f;      // P holds E4M3(P_SCALE p r)
+constexpr float P_SCALE_LOG2 = 7.0f;
+
 struct BlockK {
   float c_t, lr, inv_r;
   int ve;
@@ -162,8 +170,8 @@ __device__ __forceinline__ BlockK block_consts(float c_q, float ks, float ratio)
   }
   BlockK b;
   b.c_t = c_q * ks;
-  b.lr = 8.0f + __log2f(r);
-  b.inv_r = 1.0f / (256.0f * r);
+  b.lr = P_SCALE_LOG2 + __log2f(r);
+  b.inv_r = 1.0f / (P_SCALE * r);
   b.ve = E + 127;
   return b;
 }
@@ -183,7 +191,7 @@ struct IC {
   static constexpr int value = V;
 };
 
-constexpr float P_SLACK = 0.8f;   // log2 of the allowed growth of p above 1
+constexpr float P_SLACK = 1.8f;   // log2 of the allowed growth of p above 1: P_SCALE 2^1.8 <= 448
 
 constexpr int VMCNT(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
@@ -237,7 +245,7 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
     for (int r = 0; r < 16; ++r) pm[kb] = fmaxf(pm[kb], s[kb][r]);
   const float tm2 = wave_halves_max(fmaxf(pm[0], pm[1])) * c_t;
   // The reference moves only when the tile maximum exceeds it by more than
-  // P_SLACK (exp2 domain), so p <= 2^0.8 < 1.75 and 256 r p <= 445.7 stays
+  // P_SLACK (exp2 domain), so p <= 2^1.8 < 3.49 and 128 r p <= 445.7 stays
   // inside E4M3 range (448); moving it on every growth of any row's maximum
   // would rescale O on most early tiles.
   if (__any(tm2 > m2 + P_SLACK)) {
@@ -251,7 +259,7 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
     m2 = mnew;
   }
 
-  // P'' = 256 r exp2(c_t s - m2), quantised to E4M3 (round to nearest even);
+  // P'' = 128 r exp2(c_t s - m2), quantised to E4M3 (round to nearest even);
   // the byte for key slot e of the B operand comes from register (e / 16, e % 16)
   const float off = bk.lr - m2;
   i32x8 pq;
@@ -444,12 +452,12 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
       if (t + 1 < ntiles) step(t + 1, bk, IC<1>{});
     }
 
-    // epilogue: O = acc max s_v / (256 l) (then H / sqrt(d) for the Hadamard
+    // epilogue: O = acc max s_v / (128 l) (then H / sqrt(d) for the Hadamard
     // variant of V), LSE = ln 2 * (m2 + log2 l)
     const float ltot = wave_halves_sum(lsum);
     if (VHAD) fwht_o(acc, half);               // every lane, before the row guard: the stage pairs lanes
     if (qi < N) {
-      const float f = svmax / (256.0f * ltot) * (VHAD ? 0.08838834764831845f : 1.0f);   // 1 / sqrt(128)
+      const float f = svmax / (P_SCALE * ltot) * (VHAD ? 0.08838834764831845f : 1.0f);   // 1 / sqrt(128)
       uint16_t* orow = O + hoff + (size_t)qi * D;
       typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 #pragma unroll
