@@ -263,7 +263,7 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
   // the byte for key slot e of the B operand comes from register (e / 16, e % 16)
   const float off = bk.lr - m2;
   i32x8 pq;
-  float rs[2] = {0.0f, 0.0f};
+  float rs[2];
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     float p[4];
@@ -273,8 +273,12 @@ __device__ __forceinline__ void tile_math(const char* kt, const char* vt, const 
       p[y] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c_t, off));
       if (MASK) p[y] = sv == -INFINITY ? 0.0f : p[y];
     }
-    rs[w & 1] += (p[0] + p[1]) + (p[2] + p[3]);
-    uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    const float g = (p[0] + p[1]) + (p[2] + p[3]);
+    rs[w & 1] = w < 2 ? g : rs[w & 1] + g;
+    // the first convert fills bytes 0..1 and the second bytes 2..3, so the
+    // register's old contents do not matter: p[0]'s bits (dead after this)
+    // stand in for them and no zero has to be materialised
+    uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
     pq[w] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], b, true);
   }
   lsum += (rs[0] + rs[1]) * bk.inv_r;
