@@ -1,6 +1,8 @@
 """GPU parity of the backward pass (fa_bwd) against the fp64 oracle
 (oracle.attention_bwd) on seeded inputs: sequence lengths below one tile, at
-and around the 32-query / 64-key / 256-key tile edges and ragged, both head
+and around the tile edges (the dK/dV pass: 64-query tiles, 128-key blocks of
+four 32-key wave groups; the dQ pass: 64-key tiles, 256-query blocks) and
+ragged, both head
 dimensions, causal and not, unusual scales, and the full-size backward
 workload on sampled heads.  The GPU forward supplies O and LSE, as a caller
 would; the oracle differentiates the definition from Q, K, V and dO alone.
@@ -18,7 +20,8 @@ their sum, the same margin the forward's 2e-2 bar on O (entries of order 1)
 leaves.  The 1e-5 floor covers gradients that vanish exactly in real
 arithmetic but not in float32: with one key, dS = P (dO.V - dO.O) is zero by
 definition, while the two dot products are summed in different orders (a
-matrix instruction and the Delta pass) and differ by a few float32 ulps.
+matrix instruction and Delta's own sum in the dQ pass) and differ by a few
+float32 ulps.
 """
 import numpy as np
 import pytest
@@ -81,14 +84,15 @@ def _check(B, H, N, d, causal, seed, scale=None, heads=None, dout_scale=1.0):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 17, 32, 64, 100, 256, 257, 1000])
+@pytest.mark.parametrize("N", [1, 17, 32, 63, 64, 65, 100, 127, 128, 129, 192, 256, 257, 320, 1000])
 def test_bwd_matches_oracle(gpu, N, d, causal):
     _check(2, 3, N, d, causal, seed=N * 13 + d + int(causal))
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_several_key_blocks(gpu, causal):
-    # 2100 keys: eight full 256-key blocks, one ragged, 66 query tiles
+    # 2100 tokens: 16 full 128-key blocks and a ragged one, 33 query tiles of 64
+    # (the last ragged), 9 query blocks of 256 (the last ragged)
     _check(1, 2, 2100, 128, causal, seed=2100 + int(causal))
 
 
