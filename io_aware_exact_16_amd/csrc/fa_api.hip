@@ -253,7 +253,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   if (dtype != FA_BF16) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!sizes_ok(B, H, N, d, 16)) return FA_ERR_SHAPE;   // the Delta pass runs 16 rows per workgroup
+  if (!sizes_ok(B, H, N, d, 128)) return FA_ERR_SHAPE;   // the dK/dV pass: 128 keys per workgroup (dQ: 256 queries)
   if ((long long)N * d * 4 >= (1LL << 32)) return FA_ERR_SHAPE;   // same per-head limit as fa_fwd
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
   if (workspace_bytes < fa::attn_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_ARG;

@@ -32,8 +32,8 @@ hipError_t launch_lse_merge(const float* op, const float* lp, void* o, bool bf16
                             int d, hipStream_t stream);
 
 // Backward pass, bf16: workspace of attn_bwd_workspace_bytes(B, H, N, d) bytes
-// (LSE log2 e and Delta, float32 [B*H*N] each, and d-major bf16 copies of Q,
-// dO and K in 64-token tiles, each part 256-byte aligned).
+// (LSE log2 e and Delta, float32 [B*H*N] each, 256-byte aligned; the dQ pass
+// writes them, the dK/dV pass reads them).
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                 const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
