@@ -475,13 +475,20 @@ __global__ __launch_bounds__(DQ_NT, 1) void attn_bwd_dq_kernel(
         dp[r] = 0.0f;
       }
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc)
+      for (int dc = 0; dc < D / 16; ++dc) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *reinterpret_cast<const bf16x8*>(kt + koff[dc] + kb * KB_BYTES), qf[dc], s, 0, 0, 0);
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *reinterpret_cast<const bf16x8*>(vt + koff[dc] + kb * KB_BYTES), of[dc], dp, 0, 0, 0);
+      }
+      // keep 8 operand reads in flight ahead of the matrix ops
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8 - 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
