@@ -9,7 +9,7 @@ for the FP8 workload one fa_qkv_fp8_quant launch (Hadamard transform and
 per-block FP8 quantisation of Q and K, V quantised without the transform and
 with power-of-two block scales) followed by fa_fwd_fp8; for the decode workload one
 fa_fwd_decode call (split-KV kernel + merge); for the backward workload one
-fa_bwd call (Delta pass, dK/dV kernel, dQ kernel), with the forward's O and
+fa_bwd call (the dQ kernel, which also forms Delta, then the dK/dV kernel), with the forward's O and
 LSE computed once beforehand.  W untimed steps, then K timed
 steps bracketed by device synchronisation, timed with HIP events on the stream
 the kernels are launched on.  Prints ONE JSON line.
@@ -19,7 +19,7 @@ step; the decode workload, which is bound by reading K and V, reports its
 algorithmic HBM bytes per second against the 8 TB/s HBM peak instead; the
 backward workload counts the usual 2.5 times the forward's FLOPs (five
 products of the forward's size).  The roofline object reports the dominant
-kernel (the attention kernel; for the backward, its whole three-kernel
+kernel (the attention kernel; for the backward, its whole two-kernel
 launch sequence) against the MI355X dense matrix peak of its input type; "traffic" is the HBM
 byte count per launch measured with hardware counters (profiles/traffic.json),
 or null when that kernel's source changed since the counters were taken.
