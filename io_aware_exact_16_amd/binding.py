@@ -5,18 +5,25 @@ pointers, sizes and the current HIP stream to the C entry point of the same
 name, and raises on a negative status.  No step of the computation runs in
 Python or in torch: torch only allocates device memory and supplies the
 stream.  If libfa.so is missing or cannot be loaded the functions raise; there
-is no fallback implementation.
+is no fallback implementation.  Inside ``with debug_sync_build():`` the same
+functions call libfa_debugsync.so instead, the race-check build of the same
+sources (every LDS buffer hand-off fully serialised), whose results must equal
+libfa.so's bit for bit.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
-_lib = None
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa.so")
+_DEBUG_SYNC_PATH = os.path.join(_PKG, "libfa_debugsync.so")
+_libs = {}                 # path -> loaded library
+_active = _LIB_PATH        # the library the wrappers call
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK = 0
@@ -41,12 +48,37 @@ def library_path() -> str:
 
 def load() -> ctypes.CDLL:
     """Load libfa.so once (after torch, so both share torch's HIP runtime)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m io_aware_exact_16_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
+    return _open(_LIB_PATH)
+
+
+def load_debug_sync() -> ctypes.CDLL:
+    """Load the race-check build libfa_debugsync.so once."""
+    return _open(_DEBUG_SYNC_PATH)
+
+
+@contextlib.contextmanager
+def debug_sync_build():
+    """Route every wrapper of this module to libfa_debugsync.so inside the block."""
+    global _active
+    lib = load_debug_sync()
+    prev, _active = _active, _DEBUG_SYNC_PATH
+    try:
+        yield lib
+    finally:
+        _active = prev
+
+
+def _cur() -> ctypes.CDLL:
+    return _open(_active)
+
+
+def _open(path: str) -> ctypes.CDLL:
+    lib = _libs.get(path)
+    if lib is not None:
+        return lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m io_aware_exact_16_amd.build`")
+    lib = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, P]
     lib.fa_fwd.restype = I
@@ -74,12 +106,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 
 def fa_status_string(status: int) -> str:
-    return load().fa_status_string(int(status)).decode()
+    return _cur().fa_status_string(int(status)).decode()
 
 
 def _ptr(t):
@@ -116,7 +148,7 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool) -> None:
         _dev4(name, t, dtype, (B, H, N, d))
     if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
         raise ValueError("fa_fwd: lse must be a contiguous float32 CUDA tensor [B,H,N]")
-    st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+    st = _cur().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
                        code, _stream(q))
     _check("fa_fwd", st)
 
@@ -133,7 +165,7 @@ def fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, scale: float, caus
             raise ValueError(f"fa_fwd_fp8: {name} must be a contiguous float32 CUDA tensor [B,H,{nb}]")
     if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
         raise ValueError("fa_fwd_fp8: lse must be a contiguous float32 CUDA tensor [B,H,N]")
-    st = load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o),
+    st = _cur().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o),
                            _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), _stream(q8))
     _check("fa_fwd_fp8", st)
 
@@ -158,7 +190,7 @@ def fa_fwd_fp8_ex(q8, k8, v8, q_scale, k_scale, v_scale, q_mx, k_mx, o, lse, sca
             _dev4(name, t, torch.uint8, (B, H, N, d // 32))
     if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
         raise ValueError("fa_fwd_fp8_ex: lse must be a contiguous float32 CUDA tensor [B,H,N]")
-    st = load().fa_fwd_fp8_ex(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(q_mx),
+    st = _cur().fa_fwd_fp8_ex(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(q_mx),
                               _ptr(k_mx), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)), int(flags),
                               _stream(q8))
     _check("fa_fwd_fp8_ex", st)
@@ -175,7 +207,7 @@ def fa_mx_fp8_quant(x, x8, e8m0, hadamard: bool) -> None:
     _dev4("x", x, x.dtype)
     _dev4("x8", x8, torch.uint8, (B, H, N, d))
     _dev4("e8m0", e8m0, torch.uint8, (B, H, N, d // 32))
-    st = load().fa_mx_fp8_quant(_ptr(x), code, _ptr(x8), _ptr(e8m0), B, H, N, d, int(bool(hadamard)), _stream(x))
+    st = _cur().fa_mx_fp8_quant(_ptr(x), code, _ptr(x8), _ptr(e8m0), B, H, N, d, int(bool(hadamard)), _stream(x))
     _check("fa_mx_fp8_quant", st)
 
 
@@ -192,7 +224,7 @@ def fa_hadamard_fp8_quant(x, x8, scales, hadamard: bool) -> None:
     if not (scales.is_cuda and scales.is_contiguous() and scales.dtype == torch.float32
             and tuple(scales.shape) == (B, H, nb)):
         raise ValueError(f"fa_hadamard_fp8_quant: scales must be a contiguous float32 CUDA tensor [B,H,{nb}]")
-    st = load().fa_hadamard_fp8_quant(_ptr(x), code, _ptr(x8), _ptr(scales), B, H, N, d, int(bool(hadamard)),
+    st = _cur().fa_hadamard_fp8_quant(_ptr(x), code, _ptr(x8), _ptr(scales), B, H, N, d, int(bool(hadamard)),
                                       _stream(x))
     _check("fa_hadamard_fp8_quant", st)
 
@@ -216,14 +248,14 @@ def fa_qkv_fp8_quant(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, flags: int)
     for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
         if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and tuple(t.shape) == (B, H, nb)):
             raise ValueError(f"fa_qkv_fp8_quant: {name} must be a contiguous float32 CUDA tensor [B,H,{nb}]")
-    st = load().fa_qkv_fp8_quant(_ptr(q), _ptr(k), _ptr(v), code, _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+    st = _cur().fa_qkv_fp8_quant(_ptr(q), _ptr(k), _ptr(v), code, _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
                                  _ptr(k_scale), _ptr(v_scale), B, H, N, d, int(flags), _stream(q))
     _check("fa_qkv_fp8_quant", st)
 
 
 def fa_fwd_decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
     """Device workspace (bytes) fa_fwd_decode needs; 0 for invalid sizes.  No GPU needed."""
-    return int(load().fa_fwd_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
+    return int(_cur().fa_fwd_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
 
 
 def fa_fwd_decode(q, k, v, o, lse, scale: float, causal: bool, workspace) -> None:
@@ -241,7 +273,7 @@ def fa_fwd_decode(q, k, v, o, lse, scale: float, causal: bool, workspace) -> Non
     if not (workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("fa_fwd_decode: workspace must be a contiguous CUDA tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    st = load().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+    st = _cur().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                               int(bool(causal)), _ptr(workspace), nbytes, _stream(q))
     _check("fa_fwd_decode", st)
 
@@ -257,7 +289,7 @@ def fa_fwd_decode_noalloc(q, k, v, o, lse, scale: float, causal: bool) -> None:
     _dev4("o", o, torch.bfloat16, (B, H, Nq, d))
     if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, Nq)):
         raise ValueError("fa_fwd_decode_noalloc: lse must be a contiguous float32 CUDA tensor [B,H,Nq]")
-    st = load().fa_fwd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+    st = _cur().fa_fwd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                                       int(bool(causal)), _stream(q))
     _check("fa_fwd_decode_noalloc", st)
 
@@ -277,14 +309,14 @@ def fa_lse_merge(o_parts, lse_parts, o, lse) -> None:
     _dev4("o", o, o.dtype, (B, H, N, d))
     if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N)):
         raise ValueError("fa_lse_merge: lse must be a contiguous float32 CUDA tensor [B,H,N]")
-    st = load().fa_lse_merge(_ptr(o_parts), _ptr(lse_parts), P, B, H, N, d, _ptr(o), code, _ptr(lse),
+    st = _cur().fa_lse_merge(_ptr(o_parts), _ptr(lse_parts), P, B, H, N, d, _ptr(o), code, _ptr(lse),
                              _stream(o_parts))
     _check("fa_lse_merge", st)
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     """Device workspace (bytes) fa_bwd needs; 0 for invalid sizes.  No GPU needed."""
-    return int(load().fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+    return int(_cur().fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, workspace) -> None:
@@ -299,7 +331,7 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, worksp
     if not (workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("fa_bwd: workspace must be a contiguous CUDA tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+    st = _cur().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                        B, H, N, d, float(scale), int(bool(causal)), FA_BF16, _ptr(workspace), nbytes, _stream(q))
     _check("fa_bwd", st)
 

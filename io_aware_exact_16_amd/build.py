@@ -3,7 +3,11 @@
     python -m io_aware_exact_16_amd.build      # or: python io_aware_exact_16_amd/build.py
 
 Each HIP source is compiled in parallel to an object under _build/, then the
-objects are linked into io_aware_exact_16_amd/libfa.so.  Always recompiles.
+objects are linked into io_aware_exact_16_amd/libfa.so.  The same sources are
+also built with FA_DEBUG_SYNC defined into libfa_debugsync.so, the race-check
+build: every LDS buffer hand-off in the kernels waits for all memory
+operations and all waves, and its results must equal libfa.so's bit for bit.
+Always recompiles.
 """
 from __future__ import annotations
 
@@ -19,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+DEBUG_SYNC_LIB = os.path.join(PKG, "libfa_debugsync.so")
+DEBUG_SYNC_SUFFIX = "_debugsync"
 SOURCES = ["fa_api.hip", "attn_bf16.hip", "attn_bf16_pp.hip", "attn_decode.hip", "attn_bwd.hip", "attn_f32.hip", "attn_fp8.hip", "hadamard_fp8.hip"]
 ARCH = "gfx950"
 
@@ -34,9 +40,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug_sync: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + (DEBUG_SYNC_SUFFIX if debug_sync else "") + ".o")
+    extra = ["-DFA_DEBUG_SYNC"] if debug_sync else []
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name; that warning is expected
     noise = "is not a recognized feature for this target"
@@ -48,18 +55,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("link of libfa.so failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n" + r.stderr)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link libfa.so and its race-check twin libfa_debugsync.so; returns libfa.so's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, False) for src in SOURCES] + [(src, True) for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda job: _compile(*job), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], DEBUG_SYNC_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", DEBUG_SYNC_LIB)
     return LIB
 
 

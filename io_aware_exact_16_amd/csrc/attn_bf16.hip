@@ -138,6 +138,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's part of tile t has landed
     __syncthreads();                         // ... and every other wave's; the other buffer is free
     if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
+    FA_SYNC_POINT();
     if (CAUSAL && j0 > qw + 31) return;      // the whole tile is above this wave's diagonal
     const char* kt = reinterpret_cast<const char*>(BUF ? kb1 : kb0);
     const char* vt = reinterpret_cast<const char*>(BUF ? vb1 : vb0);

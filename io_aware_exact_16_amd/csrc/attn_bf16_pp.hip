@@ -329,6 +329,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
     const int nt2 = (ntiles + 1) & ~1;       // even: the buffers restart at 0 with every item
 
     read_q();                                // landed: waited for at the previous even boundary
+    FA_SYNC_POINT();
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -381,6 +382,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
         }
         if (j < ntiles) issue_tile(V, vcur, bh, j * BC);
       }
+      FA_SYNC_POINT();
       if ((grp == 0) == !odd) {              // matrix half
         const bool do_pv = j >= 1 && active(j - 1), do_s = active(j);
         if (do_pv && do_s) {
@@ -401,6 +403,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_pp_kernel(
             softmax_tile<false>(s, pb, acc, m2, lsum, c, j0, qi, N, half);
         }
       }
+      FA_SYNC_POINT();
     };
     for (int j = 0; j < nt2; j += 2) {
       phase(2 * j, IC<0>{});

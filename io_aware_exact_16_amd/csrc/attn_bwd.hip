@@ -305,6 +305,7 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
     __asm__ volatile("s_barrier" ::: "memory");
     if (t + 1 < ntiles) issue_tile(IC<1 - S>{}, t + 1);
+    FA_SYNC_POINT();
   };
   auto phase2 = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
@@ -317,6 +318,7 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
     p_phase1(sc, ktail || (CAUSAL && q0 < kw0 + KV_KW - 1), q0, pb);
     phase2();
     tr_products(OR(sc), pb);
+    FA_SYNC_POINT();
   };
   auto dstep = [&](auto sc, int t) __attribute__((always_inline)) {
     phase1(sc, t);
@@ -324,6 +326,7 @@ __global__ __launch_bounds__(KV_NT, 1) void attn_bwd_dkdv_kernel(
     d_phase1(sc, dpm);
     phase2();
     d_phase2(sc, dpm);
+    FA_SYNC_POINT();
   };
 
   issue_tile(IC<0>{}, 0);
@@ -523,6 +526,7 @@ __global__ __launch_bounds__(DQ_NT, 1) void attn_bwd_dq_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
     __asm__ volatile("s_barrier" ::: "memory");
     if (t + 1 < ntiles) issue_tile(j0 + BC, kn, vn);
+    FA_SYNC_POINT();
     if (CAUSAL && j0 > qw + 31) return;      // the whole tile is above this wave's diagonal
     const char* kt = reinterpret_cast<const char*>(kc);
     const char* vt = reinterpret_cast<const char*>(vc);

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(DEC_NT) void attn_decode_bf16_kernel(
     const int j0 = k0 + t * BC;
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
     if (t + 1 < ntiles) issue_tile(j0 + BC, kn, vn);
+    FA_SYNC_POINT();
     const char* kt = reinterpret_cast<const char*>(kc);
     const char* vt = reinterpret_cast<const char*>(vc);
     if ((j0 + BC > kend) || (CAUSAL && j0 + BC - 1 > qmin))

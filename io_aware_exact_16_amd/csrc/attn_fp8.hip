@@ -439,6 +439,7 @@ __global__ __launch_bounds__(NT, CAUSAL ? 3 : 2) void attn_fwd_fp8_kernel(
       __builtin_amdgcn_s_waitcnt(VMCNT(0));
       __syncthreads();
       if (t + 1 < ntiles) issue_tile(j0 + BC, IC<BUF ^ 1>{});
+      FA_SYNC_POINT();
       if (CAUSAL && j0 > qw + 31) return;
       const char* kt = reinterpret_cast<const char*>(&smem[BUF][0][0]);
       const char* vt = reinterpret_cast<const char*>(&smem[BUF][1][0]);

@@ -76,4 +76,25 @@ __device__ __forceinline__ int xcd_logical_id(int lin, int total) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Race check.  Built with FA_DEBUG_SYNC defined (libfa_debugsync.so), every
+// FA_SYNC_POINT waits for all of the wave's outstanding memory operations
+// (the DMAs it has just issued included) and then for every wave of the
+// workgroup, so each LDS buffer hand-off becomes fully serial: no DMA is in
+// flight while any wave computes.  The kernels place these points only where
+// every wave of the workgroup passes.  Both builds must give bitwise-equal
+// results; a difference means a kernel reads an LDS buffer before its data
+// has landed, or overwrites one that is still being read.  In the regular
+// build the points are empty.
+#ifdef FA_DEBUG_SYNC
+#define FA_SYNC_POINT()               \
+  do {                                \
+    __builtin_amdgcn_s_waitcnt(0);    \
+    __syncthreads();                  \
+  } while (0)
+#else
+#define FA_SYNC_POINT() \
+  do {                  \
+  } while (0)
+#endif
+
 }  // namespace fa

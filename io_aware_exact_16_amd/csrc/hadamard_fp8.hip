@@ -132,6 +132,7 @@ __global__ __launch_bounds__(2 * D) void hadamard_fp8_quant_kernel(const QuantJo
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's part of the tile (and older stores)
     __syncthreads();                         // ... every thread's part; everyone is done with nxt
     if (gblk + (int)gridDim.x < total) issue(gblk + gridDim.x, nxt);
+    FA_SYNC_POINT();
     flush();
 
     const int jo = job_of(gblk);

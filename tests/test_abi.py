@@ -39,6 +39,18 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_debug_sync_build_exports_every_declared_symbol():
+    # the race-check twin (the same sources built with FA_DEBUG_SYNC) is a drop-in replacement
+    path = os.path.join(ROOT, "io_aware_exact_16_amd", "libfa_debugsync.so")
+    if not os.path.exists(path):
+        pytest.fail("libfa_debugsync.so is not built (run `python -m io_aware_exact_16_amd.build`)")
+    dl = ctypes.CDLL(path)
+    for name in declared_functions():
+        assert hasattr(dl, name), name
+    with open(path, "rb") as f, open(os.path.join(ROOT, "io_aware_exact_16_amd", "libfa.so"), "rb") as g:
+        assert f.read() != g.read(), "the debug-sync build is identical to libfa.so"
+
+
 def test_binding_names_match_header():
     import io_aware_exact_16_amd as fa
     for name in declared_functions():
