@@ -119,3 +119,67 @@ def test_bwd(gpu, w):
         return fa.attention_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
 
     assert_bitwise_equal(w.name, both_builds(run))
+
+
+# ---------------------------------------------------------------------------
+# Grid-order independence: the same heads computed in one call (persistent work
+# lists dealt over every compute unit, heads grouped per XCD) and one head per
+# call (a different grid, a different workgroup for every item, other items
+# resident beside it) must agree bit for bit.  A kernel that let one work item
+# see another's LDS contents, or that depended on which workgroup ran an item,
+# would differ here.
+def per_head(t, b, h):
+    return t[b:b + 1, h:h + 1].contiguous()
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 8, 4096, 128, True), (1, 8, 2048, 64, False), (1, 5, 1000, 128, True)])
+def test_grid_order_fwd(gpu, B, H, N, d, causal):
+    w = custom(B, H, N, d, causal, "bf16", seed=N + d + H)
+    q, k, v = to_dev(*make_qkv(w))
+    o, lse = fa.attention(q, k, v, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            o1, lse1 = fa.attention(per_head(q, b, h), per_head(k, b, h), per_head(v, b, h), causal=causal,
+                                    scale=w.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o1.view(torch.int16), per_head(o, b, h).view(torch.int16)), (b, h)
+            assert torch.equal(lse1.view(torch.int32), per_head(lse, b, h).view(torch.int32)), (b, h)
+    log(f"[grid order] {B}x{H} heads, N={N}, d={d}, causal={causal}: one call == one call per head")
+
+
+def test_grid_order_fp8(gpu):
+    w = custom(2, 8, 4096, 128, True, "bf16", seed=4242, outlier_frac=0.001)
+    q, k, v = to_dev(*make_qkv(w))
+    (q8, qs), (k8, ks), (v8, vs) = fa.quant_qkv_fp8(q, k, v)
+    o, lse = fa.attention_fp8(q8, k8, v8, qs, ks, vs, causal=True)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for h in range(w.H):
+            (q81, qs1), (k81, ks1), (v81, vs1) = fa.quant_qkv_fp8(per_head(q, b, h), per_head(k, b, h),
+                                                                  per_head(v, b, h))
+            o1, lse1 = fa.attention_fp8(q81, k81, v81, qs1, ks1, vs1, causal=True)
+            torch.cuda.synchronize()
+            for x1, x in ((q81, q8), (k81, k8), (v81, v8)):
+                assert torch.equal(x1, per_head(x, b, h)), (b, h)
+            for s1, s in ((qs1, qs), (ks1, ks), (vs1, vs)):
+                assert torch.equal(s1.view(torch.int32), s[b:b + 1, h:h + 1].contiguous().view(torch.int32)), (b, h)
+            assert torch.equal(o1.view(torch.int16), per_head(o, b, h).view(torch.int16)), (b, h)
+            assert torch.equal(lse1.view(torch.int32), per_head(lse, b, h).view(torch.int32)), (b, h)
+    log(f"[grid order] FP8: quantiser and attention, one call == one call per head ({w.B * w.H} heads)")
+
+
+def test_grid_order_bwd(gpu):
+    w = custom(1, 6, 1000, 128, True, "bf16", seed=777, backward=True)
+    q, k, v = to_dev(*make_qkv(w))
+    do = to_dev(make_dout(w))[0]
+    o, lse = fa.attention(q, k, v, causal=True, scale=w.scale)
+    dq, dk, dv = fa.attention_bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for h in range(w.H):
+        g1 = fa.attention_bwd(per_head(q, 0, h), per_head(k, 0, h), per_head(v, 0, h), per_head(o, 0, h),
+                              per_head(lse, 0, h), per_head(do, 0, h), causal=True, scale=w.scale)
+        torch.cuda.synchronize()
+        for x1, x in zip(g1, (dq, dk, dv)):
+            assert torch.equal(x1.view(torch.int16), per_head(x, 0, h).view(torch.int16)), h
+    log(f"[grid order] backward: one call == one call per head ({w.H} heads)")
