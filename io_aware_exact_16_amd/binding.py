@@ -58,7 +58,10 @@ def load_debug_sync() -> ctypes.CDLL:
 
 @contextlib.contextmanager
 def debug_sync_build():
-    """Route every wrapper of this module to libfa_debugsync.so inside the block."""
+    """Route every wrapper of this module to libfa_debugsync.so inside the block.
+
+    The switch is process-wide (not per thread): calls made from other threads
+    while the block is open go to the debug-sync build as well."""
     global _active
     lib = load_debug_sync()
     prev, _active = _active, _DEBUG_SYNC_PATH
