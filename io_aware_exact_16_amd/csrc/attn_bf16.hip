@@ -65,7 +65,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   int qb = L - bh * nqb;
   if (CAUSAL) qb = nqb - 1 - qb;             // longest query blocks first
   const int q0 = qb * BR;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index as a scalar: the per-wave addresses and branches stay in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int qw = q0 + 32 * wave;             // first query row of this wave
   const int qi = qw + l32;                   // this lane's query
