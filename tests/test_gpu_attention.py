@@ -134,6 +134,38 @@ def test_identical_keys_give_mean_of_v(gpu, causal):
     assert (np.abs(lse - ref_lse) / np.maximum(1, np.abs(ref_lse))).max() <= 1e-3
 
 
+@pytest.mark.parametrize("N,d,causal", [(1 << 22, 128, True), (1 << 21, 64, False)])
+def test_identical_keys_at_large_sizes(gpu, N, d, causal):
+    """One head of 4M (2M) tokens: every K, V and O tensor of the head is 1 GiB (256 MiB), so tile and row byte
+    offsets reach the top of the 32-bit range the kernels address a head with.  With one key vector repeated,
+    the closed form holds at any size: O_i is the mean of the values the row sees and LSE_i = scale q_i.k + ln(count);
+    it is checked on sampled rows (reductions in float64 by torch on the device, not by the library)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(N + d)
+    q = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, 1, 1, d, generator=g, device="cuda").to(torch.bfloat16).expand(1, 1, N, d).contiguous()
+    v = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    scale = d ** -0.5
+    log(f"[large] N={N} d={d} causal={causal}: {q.numel() * 2 / 2**20:.0f} MiB per tensor")
+    o, lse = fa.attention(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 63, 64, 255, 256, 65535, 65536, N // 2 - 1, N // 2, N - 257, N - 2, N - 1}
+                  | set(torch.randint(0, N, (8,), generator=torch.Generator().manual_seed(N)).tolist()))
+    vd = v[0, 0].double()
+    k0 = k[0, 0, 0].double()
+    full_mean = vd.mean(dim=0)
+    err_o = err_l = 0.0
+    for i in rows:
+        cnt = i + 1 if causal else N
+        mean = vd[:cnt].mean(dim=0) if causal else full_mean
+        err_o = max(err_o, float((o[0, 0, i].double() - mean).abs().max()))
+        ref_l = scale * float(q[0, 0, i].double() @ k0) + float(np.log(cnt))
+        err_l = max(err_l, abs(float(lse[0, 0, i]) - ref_l) / max(1.0, abs(ref_l)))
+    log(f"  {len(rows)} rows: max|dO|={err_o:.3g} max rel dLSE={err_l:.3g}")
+    assert err_o <= 2e-2 and err_l <= 1e-3
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_single_token_returns_v(gpu, d):
     g = torch.Generator().manual_seed(6)

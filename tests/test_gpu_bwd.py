@@ -152,3 +152,29 @@ def test_bwd_identities_at_32k(gpu):
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t).all())
     assert e1 <= 1e-2 and e2 <= 1e-2 and e3 <= 1e-3
+
+
+def test_bwd_identical_keys_at_large_size(gpu):
+    """One causal head of 1M tokens (256 MiB per tensor, tile and row byte offsets near the top of the range
+    the kernels address a head with).  With one key vector repeated, P_ij = 1/(i+1) for j <= i, so the closed form
+    dV_j = sum_{i>=j} dO_i / (i+1) holds at any size; it is checked on every row, with the suffix sums taken
+    in float64 by torch on the device (not by the library).  dQ vanishes in exact arithmetic (each row of dS sums
+    to zero and every key is the same); dQ and dK must be finite."""
+    N, d = 1 << 20, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    q = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, 1, 1, d, generator=g, device="cuda").to(torch.bfloat16).expand(1, 1, N, d).contiguous()
+    v = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    do = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    scale = d ** -0.5
+    o, lse = fa.attention(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = fa.attention_bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    w = do[0, 0].double() / torch.arange(1, N + 1, device="cuda", dtype=torch.float64)[:, None]
+    dv_ref = torch.flip(torch.cumsum(torch.flip(w, [0]), 0), [0])
+    err = float((dv[0, 0].double() - dv_ref).abs().max())
+    ref = float(dv_ref.abs().max())
+    log(f"[bwd large] N={N}: max|dV - ref| = {err:.3g} (max|ref| = {ref:.3g}), max|dQ| = {float(dq.abs().max()):.3g}")
+    assert err <= 2e-2 * ref + 1e-5
+    assert bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all())
