@@ -279,3 +279,33 @@ def test_fp8_zero_v_block_and_small_v(gpu, std):
     # bounded by E4M3's own rounding, whatever V's magnitude
     assert e_ref <= min(5e-2, p_error_bound(o_emu, o_ref)) and e_emu <= 1.5e-2
     assert float((np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()) <= 1e-3
+
+
+def test_fp8_identical_keys_at_large_size(gpu):
+    """One causal head of 2M tokens through the FP8 path (the one-launch quantiser, then the FP8 kernel; every
+    E4M3 tensor of the head is 256 MiB).  With one key vector repeated every score of a row is the same, so
+    p = 1 for every visible key, the weight 128 r p is exact in E4M3 (power-of-two V scales: r = 1), and O_i is
+    the mean of the dequantised values the row sees (the oracle's decoder, sums in float64); LSE_i is
+    scale q_i.k + ln(i + 1) on the dequantised Q and K.  Checked on sampled rows."""
+    N, d = 1 << 21, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4096)
+    q = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, 1, 1, d, generator=g, device="cuda").to(torch.bfloat16).expand(1, 1, N, d).contiguous()
+    v = torch.randn(1, 1, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    scale = d ** -0.5
+    (q8, qs), (k8, ks), (v8, vs) = fa.quant_qkv_fp8(q, k, v)
+    o, lse = fa.attention_fp8(q8, k8, v8, qs, ks, vs, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    vdq = oracle.dequantize_blocks(v8.cpu().numpy(), vs.cpu().numpy())[0, 0]          # [N, d] float64
+    prefix = np.cumsum(vdq, axis=0)
+    qdq = oracle.dequantize_blocks(q8.cpu().numpy(), qs.cpu().numpy())[0, 0]
+    kdq = oracle.dequantize_blocks(k8[:, :, :1].cpu().numpy(), ks[:, :, :1].cpu().numpy())[0, 0, 0]
+    rows = sorted({0, 1, 127, 128, 65535, N // 2, N - 129, N - 1}
+                  | set(np.random.default_rng(N).integers(0, N, 8).tolist()))
+    on, ln = o[0, 0].float().cpu().numpy(), lse[0, 0].cpu().numpy()
+    err_o = max(float(np.abs(on[i] - prefix[i] / (i + 1)).max()) for i in rows)
+    err_l = max(abs(float(ln[i]) - (scale * float(qdq[i] @ kdq) + np.log(i + 1))) / max(1.0, abs(scale * float(qdq[i] @ kdq) + np.log(i + 1)))
+                for i in rows)
+    log(f"[fp8 large] N={N}: {len(rows)} rows, max|dO|={err_o:.3g} max rel dLSE={err_l:.3g}")
+    assert err_o <= 2e-2 and err_l <= 1e-3
