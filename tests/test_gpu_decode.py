@@ -129,3 +129,33 @@ def test_lse_merge_all_parts_empty(gpu):
     o, lse = fa.lse_merge(o_parts, lse_parts)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(lse == float("-inf"))
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_decode_identical_keys_at_large_size(gpu, noalloc):
+    """Four queries against 4M keys of one head (1 GiB per K and V tensor; many split-KV chunks): with one key
+    vector repeated, query i (bottom-right aligned) sees Nk - Nq + i + 1 keys with equal weight, so O_i is the
+    mean of those values and LSE_i = scale q_i.k + ln(count) (sums in float64 by torch on the device)."""
+    Nq, Nk, d = 4, 1 << 22, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    q = torch.randn(1, 1, Nq, d, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, 1, 1, d, generator=g, device="cuda").to(torch.bfloat16).expand(1, 1, Nk, d).contiguous()
+    v = torch.randn(1, 1, Nk, d, generator=g, device="cuda").to(torch.bfloat16)
+    scale = d ** -0.5
+    if noalloc:
+        o = torch.empty_like(q)
+        lse = torch.empty(1, 1, Nq, dtype=torch.float32, device="cuda")
+        fa.fa_fwd_decode_noalloc(q, k, v, o, lse, scale, True)
+    else:
+        o, lse = fa.attention_decode(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    prefix = torch.cumsum(v[0, 0].double(), dim=0)
+    err_o = err_l = 0.0
+    for i in range(Nq):
+        cnt = Nk - Nq + i + 1
+        err_o = max(err_o, float((o[0, 0, i].double() - prefix[cnt - 1] / cnt).abs().max()))
+        ref_l = scale * float(q[0, 0, i].double() @ k[0, 0, 0].double()) + float(np.log(cnt))
+        err_l = max(err_l, abs(float(lse[0, 0, i]) - ref_l) / max(1.0, abs(ref_l)))
+    log(f"[decode large] Nk={Nk} noalloc={noalloc}: max|dO|={err_o:.3g} max rel dLSE={err_l:.3g}")
+    assert err_o <= TOL["bf16"][0] and err_l <= TOL["bf16"][1]
