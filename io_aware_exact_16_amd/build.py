@@ -33,6 +33,13 @@ COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
 
 
+# Per-source compiler options.  The backward kernels are scheduled with the
+# ILP-maximising machine scheduler: 0.8 % faster per fa_bwd call on the 8k
+# causal backward (1.777 vs 1.791 ms, same GPU), with no spills; the other
+# kernels measured no difference (within 0.3 %) and keep the default.
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -43,7 +50,7 @@ def hipcc() -> str:
 def _compile(src: str, debug_sync: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + (DEBUG_SYNC_SUFFIX if debug_sync else "") + ".o")
     extra = ["-DFA_DEBUG_SYNC"] if debug_sync else []
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name; that warning is expected
     noise = "is not a recognized feature for this target"
