@@ -151,7 +151,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
 
