@@ -39,8 +39,15 @@
  *             nothing has been enqueued and the outputs are untouched, except
  *             FA_ERR_LAUNCH, which reports a failed kernel launch.  Device
  *             faults surface at the caller's next synchronisation.  NaN or Inf
- *             in the inputs is not an error; it propagates to the rows it
- *             reaches.
+ *             in the inputs is not an error; it propagates to the outputs
+ *             that depend on it (a NaN in Q or K: O and LSE of the rows whose
+ *             scores it enters; in V: that column of O in the rows that see
+ *             the key).  A non-finite V element also reaches that column in
+ *             the rows of its 64-key tile that the causal mask hides from it
+ *             (their zero weight times the value).  In the FP8 quantisers a
+ *             NaN element leaves its block's scale to the other elements and
+ *             becomes a NaN code (with the transform: its token's whole row
+ *             of codes).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -102,12 +109,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   o                 : [B,H,N,128] bfloat16 output;  lse : [B,H,N] float32 output.
  *   d                 : must be 128.
  * S = scale * (q8 k8^T) runs on FP8 matrix cores with the two block scales
- * folded into the softmax exponent.  P is quantised to E4M3 as 256 p r, where
+ * folded into the softmax exponent.  P is quantised to E4M3 as 128 p r, where
  * r in (1/2, 1] is the mantissa of the key block's V scale over the head's
  * largest, whose power of two goes into the matrix instruction's E8M0 scale of
  * the V operand (r = 1 everywhere when the V scales are powers of two, as
- * fa_qkv_fp8_quant's FA_QUANT_POW2_SCALE_V makes them); 1/256 and the largest
- * V scale are undone in float32.  (The dtype argument of fa_fwd has no room for
+ * fa_qkv_fp8_quant's FA_QUANT_POW2_SCALE_V makes them); 1/128 and the largest
+ * V scale are undone in float32.  The running reference maximum moves only when
+ * a tile's largest score exceeds it by more than 1.8 in the exp2 domain, so
+ * every p <= 2^1.8 and 128 p r <= 445.7 stays in E4M3's range (448).  (The dtype argument of fa_fwd has no room for
  * the block scales, hence a separate entry point.)
  */
 int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,

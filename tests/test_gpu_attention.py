@@ -10,7 +10,7 @@ import io_aware_exact_16_amd as fa
 import oracle
 from io_aware_exact_16_amd.workloads import WORKLOADS, custom, make_qkv
 
-from gpu_helpers import compare, compare_sampled, f64, log, run_attention, sample_rows, to_dev
+from gpu_helpers import TOL, compare, compare_sampled, f64, log, run_attention, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -264,3 +264,38 @@ def test_error_status_with_device_tensors(gpu):
     assert e.value.status == -6
     torch.cuda.synchronize()
     assert torch.all(o == 7.0) and torch.all(lse == 7.0)      # outputs untouched on error
+
+
+# ---------------------------------------------------------------------------
+# NaN in the inputs is not an error: it reaches exactly the outputs that depend on it
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False), (128, False)])
+def test_nan_reaches_only_dependent_outputs(gpu, d, causal):
+    N, jk, jq, jv, cv = 300, 150, 77, 200, 5
+    w = custom(1, 2, N, d, causal, "bf16", seed=400 + d)
+    q, k, v = make_qkv(w)
+    nan = float("nan")
+    q[0, 0, jq, 3] = nan          # one element of query row jq, head 0
+    k[0, 1, jk, 7] = nan          # one element of key jk, head 1
+    v[0, 0, jv, cv] = nan         # one element of value jv, column cv, head 0
+    o, lse = run_attention(q, k, v, causal, w.scale)
+    qc, kc, vc = q.clone(), k.clone(), v.clone()
+    qc[0, 0, jq, 3] = 0.0
+    kc[0, 1, jk, 7] = 0.0
+    vc[0, 0, jv, cv] = 0.0
+    o_ref, lse_ref = oracle.attention(f64(qc), f64(kc), f64(vc), w.scale, causal)
+    rows = np.arange(N)
+    # rows that see value jv, and (causal) the rows of its 64-key tile that the mask hides from it: their
+    # zero weight times the NaN in the matrix product
+    sees = (rows >= 64 * (jv // 64)) if causal else np.ones(N, bool)
+    sees_k = (rows >= jk) if causal else np.ones(N, bool)               # rows that see key jk
+    nan_o = np.zeros(o.shape, bool)
+    nan_l = np.zeros(lse.shape, bool)
+    nan_o[0, 0, jq, :] = True                                           # a NaN query: its whole row
+    nan_l[0, 0, jq] = True
+    nan_o[0, 0, sees, cv] = True                                        # a NaN value: its column, in rows that see it
+    nan_o[0, 1, sees_k, :] = True                                       # a NaN key: whole rows that see it
+    nan_l[0, 1, sees_k] = True
+    assert np.isnan(o[nan_o]).all() and np.isnan(lse[nan_l]).all()
+    assert np.isfinite(o[~nan_o]).all() and np.isfinite(lse[~nan_l]).all()
+    assert np.abs(o[~nan_o] - o_ref[~nan_o]).max() <= TOL["bf16"][0]
+    assert (np.abs(lse[~nan_l] - lse_ref[~nan_l]) / np.maximum(1, np.abs(lse_ref[~nan_l]))).max() <= TOL["bf16"][1]

@@ -143,3 +143,32 @@ def test_pow2_v_scales(gpu, N, hadamard_v):
         np.testing.assert_array_equal(v8.cpu().numpy(), rc)
     for x8, s, x in ((q8, qs, q), (k8, ks, k)):
         assert check_fp8_codes(x, x8.cpu().numpy(), s.cpu().numpy(), True) <= 1e-3 * x8.numel() + 1
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_nan_element(gpu, hadamard):
+    """A NaN element is ignored by its block's scale (the largest magnitude) and turns into NaN codes: its own
+    code, or with the transform every code of its token's row.  Every other code and every scale equal those of
+    the same input with that element's whole row replaced by zeros, as long as that row does not hold the block's
+    largest magnitude (a zero row and a NaN row both leave the maximum to the other rows)."""
+    x = make_qkv(custom(1, 2, 300, 128, False, "bf16", seed=31))[0]
+    r, c = 70, 9                                   # block 0 of head 0; a row that does not hold the block maximum
+    xz = x.clone()
+    xz[0, 0, r, :] = 0.0
+    xn = xz.clone()
+    xn[0, 0, r, c] = float("nan")
+    codes = []
+    for t in (xz, xn):
+        c8, s = fa.quant_fp8(t.to("cuda"), hadamard=hadamard)
+        torch.cuda.synchronize()
+        codes.append((c8.cpu().numpy(), s.cpu().numpy()))
+    (cz, sz), (cn, sn) = codes
+    assert np.isfinite(sn).all() and np.array_equal(sn, sz)
+    is_nan = (cn & 0x7F) == 0x7F                   # E4M3 NaN: exponent and mantissa all ones
+    want = np.zeros(cn.shape, bool)
+    if hadamard:
+        want[0, 0, r, :] = True
+    else:
+        want[0, 0, r, c] = True
+    assert np.array_equal(is_nan, want)
+    assert np.array_equal(cn[~want], cz[~want])
