@@ -44,7 +44,9 @@
  *             scores it enters; in V: that column of O in the rows that see
  *             the key).  A non-finite V element also reaches that column in
  *             the rows of its 64-key tile that the causal mask hides from it
- *             (their zero weight times the value).  In the FP8 quantisers a
+ *             (their zero weight times the value).  In fa_bwd a non-finite
+ *             input can likewise reach the gradients of the other rows and
+ *             keys of its tiles.  In the FP8 quantisers a
  *             NaN element leaves its block's scale to the other elements and
  *             becomes a NaN code (with the transform: its token's whole row
  *             of codes).
