@@ -309,3 +309,38 @@ def test_fp8_identical_keys_at_large_size(gpu):
                 for i in rows)
     log(f"[fp8 large] N={N}: {len(rows)} rows, max|dO|={err_o:.3g} max rel dLSE={err_l:.3g}")
     assert err_o <= 2e-2 and err_l <= 1e-3
+
+
+def test_fp8_nan_reaches_only_dependent_outputs(gpu):
+    """The FP8 path (one-launch quantiser, transform on Q and K, then the FP8 kernel): a NaN element of Q makes
+    its row's output and LSE NaN; one of K the rows that see that key; one of V (no transform on V) that column
+    in the rows that see the key and in the rows of its 64-key tile that the causal mask hides from it.  All
+    other outputs are finite and equal the run with those three rows replaced by zeros (identical codes and scales
+    elsewhere, so bit for bit)."""
+    N, jq, jk, jv, cv = 300, 77, 150, 200, 5
+    q, k, v = make_qkv(custom(1, 2, N, 128, True, "bf16", seed=4321))
+    for t, h, j in ((q, 0, jq), (k, 1, jk), (v, 0, jv)):
+        t[0, h, j, :] = 0.0                       # zero rows: neither they nor a NaN in them set a block's scale
+    runs = []
+    for with_nan in (False, True):
+        qq, kk, vv = q.clone(), k.clone(), v.clone()
+        if with_nan:
+            qq[0, 0, jq, 3] = float("nan")
+            kk[0, 1, jk, 7] = float("nan")
+            vv[0, 0, jv, cv] = float("nan")
+        (q8, qs), (k8, ks), (v8, vs) = fa.quant_qkv_fp8(qq.to("cuda"), kk.to("cuda"), vv.to("cuda"))
+        o, lse = fa.attention_fp8(q8, k8, v8, qs, ks, vs, causal=True)
+        torch.cuda.synchronize()
+        runs.append((o.float().cpu().numpy(), lse.cpu().numpy()))
+    (o0, l0), (o1, l1) = runs
+    rows = np.arange(N)
+    nan_o = np.zeros(o1.shape, bool)
+    nan_l = np.zeros(l1.shape, bool)
+    nan_o[0, 0, jq, :] = True
+    nan_l[0, 0, jq] = True
+    nan_o[0, 1, rows >= jk, :] = True
+    nan_l[0, 1, rows >= jk] = True
+    nan_o[0, 0, rows >= 64 * (jv // 64), cv] = True
+    assert np.isnan(o1[nan_o]).all() and np.isnan(l1[nan_l]).all()
+    assert np.isfinite(o1[~nan_o]).all() and np.isfinite(l1[~nan_l]).all()
+    assert np.array_equal(o1[~nan_o], o0[~nan_o]) and np.array_equal(l1[~nan_l], l0[~nan_l])
