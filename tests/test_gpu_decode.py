@@ -159,3 +159,39 @@ def test_decode_identical_keys_at_large_size(gpu, noalloc):
         err_l = max(err_l, abs(float(lse[0, 0, i]) - ref_l) / max(1.0, abs(ref_l)))
     log(f"[decode large] Nk={Nk} noalloc={noalloc}: max|dO|={err_o:.3g} max rel dLSE={err_l:.3g}")
     assert err_o <= TOL["bf16"][0] and err_l <= TOL["bf16"][1]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_attention_shards_on_one_gpu(gpu, causal):
+    """The sharded decomposition ring attention would run across devices, emulated on one GPU: the sequence is
+    cut into 4 shards; query shard i attends to every key shard j (causal: j < i in full, j = i with the causal
+    mask, j > i not at all) with fa_fwd, and fa_lse_merge combines the partial (O, LSE) of each query shard.  The
+    result matches the float64 oracle on the whole sequence at the bf16 tolerances."""
+    g, B, H, N, d = 4, 1, 4, 2048, 128
+    w = custom(B, H, N, d, causal, "bf16", seed=606)
+    q, k, v = to_dev(*make_qkv(w))
+    n = N // g
+    outs, lses = [], []
+    for i in range(g):
+        qi = q[:, :, i * n:(i + 1) * n].contiguous()
+        parts_o = torch.zeros(g, B, H, n, d, dtype=torch.float32, device="cuda")
+        parts_l = torch.full((g, B, H, n), float("-inf"), dtype=torch.float32, device="cuda")
+        for j in range(g):
+            if causal and j > i:
+                continue                        # a shard of later keys: an empty part (LSE = -inf)
+            kj = k[:, :, j * n:(j + 1) * n].contiguous()
+            vj = v[:, :, j * n:(j + 1) * n].contiguous()
+            o, lse = fa.attention(qi, kj, vj, causal=causal and j == i, scale=w.scale)
+            parts_o[j] = o.float()
+            parts_l[j] = lse
+        o_i, lse_i = fa.lse_merge(parts_o, parts_l)
+        outs.append(o_i)
+        lses.append(lse_i)
+    torch.cuda.synchronize()
+    o_all = torch.cat(outs, dim=2).double().cpu().numpy()
+    lse_all = torch.cat(lses, dim=2).double().cpu().numpy()
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), w.scale, causal)
+    err_o = float(np.abs(o_all - o_ref).max())
+    err_l = float((np.abs(lse_all - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max())
+    log(f"[ring emulation] {g} shards, causal={causal}: max|dO|={err_o:.3g} max rel dLSE={err_l:.3g}")
+    assert err_o <= TOL["bf16"][0] and err_l <= TOL["bf16"][1]
